@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+One step = the whole decode hot path over one batch: KV append of each
+sequence's new token at its explicit position, then paged decode attention
+(split-KV first pass + log-sum-exp combine) over the block-paged cache.
+
+Default workload: 256 sequences, bf16 K/V, 32 query heads over 8 KV heads,
+head_dim 128, block size 16, context lengths lognormal (median 1024, max
+8192), blocks randomly scattered over a pool of 1.2x the tokens (seeded,
+synthetic).  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  ``value`` is the step's achieved HBM throughput in GB/s
+from algorithmic bytes (K/V of every attended token, q, out, lse, block-table
+entries, lengths, and the appended rows).  ``roofline`` is the first-pass
+kernel alone, timed with HIP events on the stream it runs on.
+``cpu_baseline`` is the float64 CPU oracle on the same inputs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_high_concurrency.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", "paged_decode.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="high_concurrency",
+                   choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--partition-size", type=int, default=512)
+    p.add_argument("--kernel-reps", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time for the oracle baseline (repeats the whole batch)")
+    p.add_argument("--no-copy-probe", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic_bytes(case, append_tokens: int):
+    """Bytes the decode path must move: (decode, append)."""
+    eb = case.elem_bytes
+    B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    ctx = case.context_lens.astype("int64")
+    kv = int(ctx.sum()) * 2 * hkv * d * eb
+    per_seq = B * (hq * d * eb + hq * d * 4 + hq * 4 + 4) + int(((ctx + 15) // 16).sum()) * 4
+    decode = kv + per_seq
+    # append: read k_new/v_new, write the cache rows, start_pos + cu + one table entry each
+    append = append_tokens * (2 * 2 * hkv * d * eb + 4 * 3)
+    return decode, append
+
+
+def copy_probe(torch, nbytes=2 << 30, reps=10):
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    sec = s.elapsed_time(e) / 1e3 / reps
+    del a, b
+    return 2 * nbytes / sec / 1e9
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from committed PMC counters, if taken on this kernel source."""
+    try:
+        info = json.load(open(TRAFFIC_FILE))
+        digest = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if info.get("kernel_source_sha256") == digest:
+            return info.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(case, decode_bytes, target_s):
+    import numpy as np  # noqa: F401
+    import oracle.paged_attention as pa
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    reps, t_total = 0, 0.0
+    while reps == 0 or (t_total < target_s and reps < 5):
+        t0 = time.perf_counter()
+        pa.paged_decode(case.q[0], case.k_pool[0], case.v_pool[0], case.block_tables,
+                        case.context_lens, case.scale, case.kv_dtype)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    sec = t_total / reps
+    return {
+        "value": round(decode_bytes / sec / 1e9, 3),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"whole {case.name} batch ({case.batch} sequences, sum ctx "
+                   f"{int(case.context_lens.sum())}), decode only, float64 numpy, {reps} rep(s), "
+                   f"{sec:.2f} s each; host affinity {len(os.sched_getaffinity(0))} cpus"),
+        "seq_tokens_per_s": round(float(case.context_lens.sum()) / sec, 1),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this decode path has no "
+              "multi-GPU mode; sharding by sequence or KV head needs no collective.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_kv_cache_200_amd as pkv
+    from workloads import bf16_bits, config_case, parallel_normal
+
+    print(f"[bench] building inputs: {args.workload} seed {args.seed}", file=sys.stderr, flush=True)
+    case = config_case(args.workload, args.seed)
+    P = case.extra.get("partition_size", args.partition_size)
+    B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            x = x.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    q = to_dev(case.q[0])
+    kc = to_dev(case.k_pool[0])
+    vc = to_dev(case.v_pool[0])
+    tables = to_dev(case.block_tables)
+    ctx = to_dev(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    # the token appended this step sits at position ctx - 1 (it attends to itself)
+    ss = np.random.SeedSequence(entropy=args.seed, spawn_key=(99,))
+    kn = parallel_normal(ss.spawn(1)[0], (B, hkv, d))
+    vn = parallel_normal(ss.spawn(1)[0], (B, hkv, d))
+    if case.kv_dtype == "bf16":
+        kn, vn = bf16_bits(kn), bf16_bits(vn)
+    k_new, v_new = to_dev(kn), to_dev(vn)
+    start = to_dev((case.context_lens - 1).clip(min=0).astype(np.int32))
+    cu = to_dev(np.arange(B + 1, dtype=np.int32))
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+    ws_bytes = pkv.decode_workspace_bytes(B, hq, d, max_ctx, P)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    scale = float(case.scale)
+
+    def step():
+        pkv.kv_append(kc, vc, k_new, v_new, tables, start, cu)
+        pkv.paged_decode(q, kc, vc, tables, ctx, max_ctx, scale=scale, partition_size=P, out=out,
+                         lse=lse, workspace=ws)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
+
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+
+    # the first pass alone: same kernel and partitioning, partial outputs only
+    np_max = max(1, -(-max_ctx // P)) if P > 0 else 1
+    part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
+
+    def pass1():
+        pkv.paged_decode_partials(q, kc, vc, tables, ctx, max_ctx, P, scale=scale,
+                                  part_out=part_out, part_lse=part_lse)
+
+    for _ in range(5):
+        pass1()
+    torch.cuda.synchronize()
+    ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ks.record(stream)
+    for _ in range(args.kernel_reps):
+        pass1()
+    ke.record(stream)
+    torch.cuda.synchronize()
+    pass1_s = ks.elapsed_time(ke) / 1e3 / args.kernel_reps
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
+
+    decode_bytes, append_bytes = algorithmic_bytes(case, B)
+    step_s = ms_per_step / 1e3
+    value = (decode_bytes + append_bytes) / step_s / 1e9
+    # pass 1 moves the decode bytes except the final out/lse, plus its partial results
+    p1_bytes = decode_bytes
+    achieved = p1_bytes / pass1_s / 1e9
+    traffic = traffic_from_profile()
+
+    probe = None if args.no_copy_probe else copy_probe(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, decode_bytes, args.cpu_seconds)
+
+    sum_ctx = int(case.context_lens.sum())
+    line = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) + seq-tokens/s at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "seed": args.seed,
+            "batch": B,
+            "num_q_heads": hq,
+            "num_kv_heads": hkv,
+            "head_dim": d,
+            "block_size": 16,
+            "sum_context_tokens": sum_ctx,
+            "max_context_len": max_ctx,
+            "num_blocks": case.num_blocks,
+            "partition_size": P,
+            "step": "kv_append(1 token/seq) + paged_decode(split-KV pass 1 + LSE combine)",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "seq_tokens_per_s": round(sum_ctx / step_s, 1),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, p)), 5) for p in (10, 50, 90)],
+        "algorithmic_bytes_per_step": decode_bytes + append_bytes,
+        "roofline": {
+            "kernel": "decode_pass1_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": p1_bytes,
+            "avg_launch_us": round(pass1_s * 1e6, 2),
+        },
+        "copy_probe_gbps": None if probe is None else round(probe, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

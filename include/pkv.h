@@ -1,0 +1,219 @@
+/*
+ * pkv.h - single-token decode attention over a block-paged KV cache, for AMD
+ * Instinct MI355X (gfx950).  C ABI; every entry point is extern "C".
+ *
+ * The problem, as the pages state it:
+ *   - spindle, "Paging": each sequence's keys/values live in fixed-size blocks
+ *     (16 tokens) drawn from a shared pool and are addressed through a
+ *     per-sequence block table; forked sequences share blocks copy-on-write
+ *     through reference counts.
+ *   - spindle, "Two bugs worth recording": append takes an explicit start
+ *     position, gather takes an explicit length, and the caller (not the
+ *     cache) advances lengths, once per step.  Nothing here ever infers or
+ *     advances a length.
+ *   - mlsystems topic listing, flash-decoding entry: at q_len = 1 the KV
+ *     length is split into partitions processed in parallel, whose partial
+ *     results are merged afterwards (log-sum-exp combine).
+ *
+ * Layout (one transformer layer; every call works on one layer's caches):
+ *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ *                      elements of `dtype`, contiguous.  Block b, KV head h
+ *                      is one contiguous run of block_size * head_dim
+ *                      elements.
+ *   block_tables     : int32 [batch][bt_stride], row s = sequence s's
+ *                      physical block ids in logical order; each row holds
+ *                      bt_stride entries, so a sequence can hold at most
+ *                      bt_stride * block_size tokens.
+ *   context_lens     : int32 [batch], tokens each sequence attends to.
+ *   q                : [batch][num_q_heads][head_dim] of `dtype`.
+ *   out              : float32 [batch][num_q_heads][head_dim].
+ *   lse              : float32 [batch][num_q_heads], natural-log
+ *                      log-sum-exp of the scaled scores.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Pointers are device pointers unless marked "host".  The caller owns and
+ * allocates every buffer (workspace included); the library allocates no
+ * device memory and keeps no state between calls.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream) and returns without
+ * synchronising; buffers must stay alive until the stream has finished.
+ *
+ * Errors: each call returns PKV_OK (0) or a negative PKV_ERR_* code after
+ * checking its host-side arguments; nothing is enqueued on error.  Device
+ * data (block ids, positions, lengths) is checked by the kernels themselves:
+ * an out-of-range value is never dereferenced; the offending unit is skipped
+ * or clamped and a bit is set in a per-device error word that
+ * pkv_device_error() reads back.  Outputs of a call that set such a bit are
+ * unspecified.
+ *
+ * Supported shapes: block_size 16; head_dim 64 or 128; num_q_heads a
+ * multiple of num_kv_heads with a group size of 1..8; partition_size 0 or a
+ * multiple of 16.  dtype PKV_F32 or PKV_BF16 (bfloat16 bit patterns).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* pkv_stream_t; /* hipStream_t */
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,          /* a required pointer is NULL                     */
+  PKV_ERR_DTYPE = -2,         /* unknown dtype                                  */
+  PKV_ERR_SHAPE = -3,         /* unsupported size/shape combination             */
+  PKV_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required     */
+  PKV_ERR_LAUNCH = -5,        /* the HIP runtime rejected a launch              */
+  PKV_ERR_DEVICE = -6,        /* a HIP runtime call failed                      */
+  PKV_ERR_OUT_OF_BLOCKS = -7, /* block manager: pool exhausted (nothing changed)*/
+  PKV_ERR_ARG = -8            /* bad argument value (alignment, range, id)      */
+};
+
+/* Bits of the device error word. */
+enum pkv_device_error_bits {
+  PKV_DEVERR_BLOCK_ID = 1,      /* a block-table entry outside [0, num_blocks)   */
+  PKV_DEVERR_POSITION = 2,      /* an append position outside the table row      */
+  PKV_DEVERR_CONTEXT = 4,       /* context_lens[s] < 0 or > bt_stride*block_size */
+  PKV_DEVERR_MAX_CONTEXT = 8,   /* context_lens[s] > the max_context_len given   */
+  PKV_DEVERR_CU = 16            /* cu_new_tokens not non-decreasing / bad total  */
+};
+
+/* Library version, e.g. 100 for 1.0.0. */
+int pkv_version(void);
+
+/* Static description of a status code. Never NULL. */
+const char* pkv_status_string(int status);
+
+/*
+ * KV append (spindle, "Two bugs worth recording": append takes an explicit
+ * start position).
+ *
+ * For each sequence s and i in [0, cu_new_tokens[s+1] - cu_new_tokens[s]):
+ *   pos = start_pos[s] + i,
+ *   block = block_tables[s][pos / block_size], slot = pos % block_size,
+ *   k_cache[block][h][slot][:] = k_new[cu_new_tokens[s] + i][h][:]  for every
+ *   KV head h, and the same for v.
+ * A bit-exact copy; no other cache element is written; no length is read or
+ * advanced.  The target blocks must be exclusively owned by s (copy-on-write
+ * already resolved) and distinct across sequences, otherwise writes race.
+ *
+ *   k_new, v_new    : [total_new][num_kv_heads][head_dim] of dtype.
+ *   start_pos       : int32 [batch].
+ *   cu_new_tokens   : int32 [batch + 1], cu[0] = 0, non-decreasing,
+ *                     cu[batch] = total_new.
+ * total_new = 0 is a no-op.
+ */
+int pkv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  const int32_t* block_tables, int64_t bt_stride, const int32_t* start_pos,
+                  const int32_t* cu_new_tokens, int32_t batch, int32_t total_new,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t dtype, pkv_stream_t stream);
+
+/*
+ * Bytes of device workspace pkv_paged_decode needs: the per-partition
+ * partial outputs and log-sum-exps, batch * num_q_heads * P * (head_dim + 1)
+ * floats (plus alignment) with P = ceil(max_context_len / partition_size).
+ * 0 when partition_size is 0 or a single partition covers max_context_len.
+ */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Paged decode attention (spindle: gather by block table with an explicit
+ * length, then attend; flash-decoding split for long contexts).
+ *
+ * For each sequence s with n = context_lens[s] and each query head h
+ * (KV head kh = h / G):
+ *   score_t = scale * dot(q[s][h], K_s[kh][t]),  t in [0, n),
+ *   out[s][h] = sum_t softmax(score)_t * V_s[kh][t],
+ *   lse[s][h] = ln sum_t exp(score_t),
+ * where K_s[kh][t] = k_cache[block_tables[s][t / 16]][kh][t % 16].
+ * n = 0 gives out = 0 and lse = -inf.  Slots at or past n (the unused tail
+ * of the last block, stale or NaN data) never influence the result.
+ *
+ * max_context_len (host) must be >= every context_lens[s]; it sizes the grid
+ * so that no device-to-host synchronisation is needed.
+ * partition_size = 0: one pass per (sequence, KV head) over the whole
+ * context.  partition_size = P > 0 (multiple of 16): the context is split
+ * into partitions of P tokens, each attended independently, then merged by
+ * their log-sum-exps (a second kernel on the same stream); sequences that
+ * fit in one partition are written directly.  The result does not depend on
+ * the batch: a sequence decoded alone or in any batch, with the same
+ * partition_size, gives bit-identical out and lse.
+ * lse may be NULL.  workspace may be NULL when
+ * pkv_decode_workspace_bytes(...) is 0.
+ */
+int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
+                     const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_context_len, float scale,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     int32_t dtype, pkv_stream_t stream);
+
+/*
+ * First pass only: per-partition attention, no merge.
+ *   part_out : float32 [batch][num_q_heads][max_partitions][head_dim]
+ *   part_lse : float32 [batch][num_q_heads][max_partitions]
+ * Partition p of sequence s covers tokens [p*P, min((p+1)*P, n)); its entry
+ * holds that range's normalised attention output and log-sum-exp.  For
+ * n = 0, entry 0 is out = 0, lse = -inf.  Entries p >= max(1, ceil(n / P))
+ * are not written (pkv_lse_combine never reads them).  Exactly one kernel
+ * is launched: the first pass of pkv_paged_decode.
+ * Requires max_partitions >= ceil(max_context_len / partition_size) >= 1
+ * and partition_size > 0.
+ */
+int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int64_t bt_stride,
+                              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t partition_size, int32_t max_partitions, int32_t dtype,
+                              pkv_stream_t stream);
+
+/*
+ * Second pass: merge partitions by log-sum-exp (flash-decoding combine).
+ * For each (s, h), over p < ceil(context_lens[s] / partition_size) with
+ * part_lse > -inf:  M = max lse_p, w_p = exp(lse_p - M),
+ *   out = sum w_p part_out_p / sum w_p,  lse = M + ln sum w_p;
+ * no live partition gives out = 0, lse = -inf.  Layouts as in
+ * pkv_paged_decode_partials.  lse may be NULL.
+ */
+int pkv_lse_combine(float* out, float* lse, const float* part_out, const float* part_lse,
+                    const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                    int32_t head_dim, int32_t partition_size, int32_t max_partitions,
+                    pkv_stream_t stream);
+
+/*
+ * Copy-on-write block copy (spindle, "Paging": reference counts give
+ * copy-on-write forking).  For i in [0, n) and every layer l in
+ * [0, num_layers):  block dst[i] := block src[i] (all KV heads, all slots)
+ * in both caches, bit-exact.  Layer l's caches start layer_stride elements
+ * after layer l-1's (layer_stride is ignored when num_layers = 1).
+ * src and dst are int32 [n] device arrays; the dst ids must be distinct and
+ * disjoint from the src ids (otherwise copies race).
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                    int32_t n, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t num_layers, int64_t layer_stride, int32_t dtype,
+                    pkv_stream_t stream);
+
+/*
+ * Synchronises `stream`, then returns (in *flags, host) and clears the
+ * current device's error word: an OR of PKV_DEVERR_* bits set by kernels
+ * since the last call.  Returns PKV_OK or PKV_ERR_DEVICE.
+ */
+int pkv_device_error(pkv_stream_t stream, int32_t* flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,23 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over ``libpkv.so`` (C ABI in ``include/pkv.h`` and
+``include/pkv_block_manager.h``): argument marshalling only, every step of the
+path runs in the library's HIP kernels or its native block manager.  The
+library must be built first (``python -m paged_kv_cache_200_amd.build``);
+using the ops without it raises.
+"""
+
+from .ops import (  # noqa: F401
+    BLOCK_SIZE,
+    copy_blocks,
+    decode_workspace_bytes,
+    describe_device_error,
+    device_error,
+    kv_append,
+    lse_combine,
+    paged_decode,
+    paged_decode_partials,
+)
+from .block_manager import BlockManager, OutOfBlocks  # noqa: F401
+
+__version__ = "1.0.0"

@@ -1,0 +1,601 @@
+// Paged decode attention for gfx950: first pass (per KV partition) and the
+// log-sum-exp combine.
+//
+// What is computed (spindle, "Paging" and "Two bugs worth recording"): for a
+// sequence with explicit length n, gather the K/V of tokens [0, n) through
+// its block table and run softmax attention of the single query token
+// against them.  Long contexts are split flash-decoding style (mlsystems topic
+// listing, flash-decoding entry): each KV partition is attended on its own
+// and the partial results are merged by their log-sum-exps.
+//
+// Work decomposition.  One workgroup = (sequence, KV head, partition), four
+// wavefronts.  Every query head of the KV head's GQA group is handled by the
+// same workgroup, so each K/V byte is read from HBM once per call.  Wave w
+// takes the partition's blocks w, w+4, w+8, ...; one 16-token block of one KV
+// head is a contiguous 16*D run, read whole with 16-byte loads.
+//
+// Inside a wave, 8 lanes share one token: a lane holds D/8 elements of that
+// token (two 16-byte chunks for bf16 D=128), so a block is 2 tokens per lane.
+// The QK dot product is a per-lane partial (bf16 pairs through the dot2
+// instruction, fp32 through FMA) finished by a 3-step DPP sum over the 8
+// lanes.  Each 8-lane group keeps its own online-softmax state (max m, sum l,
+// accumulator over its dims) for every query head of the group, so the hot
+// loop needs no other cross-lane traffic.  The running max is lazy: it is
+// only raised when a score exceeds it by more than 2^8, which keeps the
+// accumulator rescale off the common path while all exponentials stay <= 2^8.
+// At the end the 8 groups of a wave are merged with lane shuffles and the 4
+// waves through LDS, by the same log-sum-exp rule as the combine.
+//
+// Scores are kept in log2 units (scale * log2(e) folded in) so every
+// exponential is one v_exp_f32.
+
+#include "common.h"
+
+PKV_DEFINE_ERROR_WORD(decode)
+
+namespace pkv {
+namespace {
+
+constexpr int kLanesPerToken = 8;
+constexpr int kGroups = kWave / kLanesPerToken;  // token groups per wave
+constexpr int kWaves = 4;                        // wavefronts per workgroup
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLazyMaxSlack = 8.0f;            // log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T, int D>
+struct Geom {
+  static constexpr int kChunkElems = 16 / static_cast<int>(sizeof(T));  // elems per 16 B
+  static constexpr int kChunks = D * static_cast<int>(sizeof(T)) / (16 * kLanesPerToken);
+  static constexpr int kElems = kChunks * kChunkElems;                   // elems per lane
+  static constexpr int kWords = kChunks * 4;                             // 32-bit words per lane
+  static constexpr int kChunkStride = kLanesPerToken * kChunkElems;     // elems between chunks
+  static_assert(kChunks >= 1, "head_dim too small for 8 lanes per token");
+};
+
+// Dimension held by element e of a lane with sub-index `sub` (0..7).
+template <typename T, int D>
+__device__ __forceinline__ int lane_dim(int sub, int e) {
+  using Gm = Geom<T, D>;
+  return (e / Gm::kChunkElems) * Gm::kChunkStride + sub * Gm::kChunkElems + (e % Gm::kChunkElems);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ float dot_word(uint32_t qw, uint32_t kw, float acc);
+
+template <>
+__device__ __forceinline__ float dot_word<uint16_t>(uint32_t qw, uint32_t kw, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw),
+                                         __builtin_bit_cast(bf16x2_t, kw), acc, false);
+}
+
+template <>
+__device__ __forceinline__ float dot_word<float>(uint32_t qw, uint32_t kw, float acc) {
+  return fmaf(__uint_as_float(qw), __uint_as_float(kw), acc);
+}
+
+// Widen the words of one token's chunks to float32 values, in element order.
+template <typename T, int D>
+__device__ __forceinline__ void widen(const uint32_t (&w)[Geom<T, D>::kWords],
+                                      float (&v)[Geom<T, D>::kElems]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int j = 0; j < Geom<T, D>::kWords; ++j) {
+      v[2 * j] = bf16_lo(w[j]);
+      v[2 * j + 1] = bf16_hi(w[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < Geom<T, D>::kWords; ++j) v[j] = __uint_as_float(w[j]);
+  }
+}
+
+template <typename T, int D>
+struct TokenRegs {
+  uint32_t k[2][Geom<T, D>::kWords];  // [token in block: grp, grp+8][words]
+  uint32_t v[2][Geom<T, D>::kWords];
+};
+
+template <typename T, int D, int G>
+struct GroupState {
+  float m[G];                       // lazy running max, log2 units
+  float l[G];                       // sum of exp2(score - m)
+  float acc[G][Geom<T, D>::kElems]; // sum of exp2(score - m) * V over this lane's dims
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_block(TokenRegs<T, D>& r, const T* __restrict__ kt,
+                                           const T* __restrict__ vt, int lane_off) {
+  using Gm = Geom<T, D>;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int c = 0; c < Gm::kChunks; ++c) {
+      const int off = lane_off + i * kGroups * D + c * Gm::kChunkStride;
+      const uint4 kk = *reinterpret_cast<const uint4*>(kt + off);
+      const uint4 vv = *reinterpret_cast<const uint4*>(vt + off);
+      r.k[i][4 * c + 0] = kk.x; r.k[i][4 * c + 1] = kk.y;
+      r.k[i][4 * c + 2] = kk.z; r.k[i][4 * c + 3] = kk.w;
+      r.v[i][4 * c + 0] = vv.x; r.v[i][4 * c + 1] = vv.y;
+      r.v[i][4 * c + 2] = vv.z; r.v[i][4 * c + 3] = vv.w;
+    }
+  }
+}
+
+// One 16-token block: 2 tokens per lane (token grp and grp + 8 of the block).
+// kMasked: only the first n_valid tokens of the block count.
+template <typename T, int D, int G, bool kMasked>
+__device__ __forceinline__ void process_block(const TokenRegs<T, D>& r,
+                                              const uint32_t (&q)[G][Geom<T, D>::kWords],
+                                              GroupState<T, D, G>& st, float scale_log2,
+                                              int grp, int n_valid) {
+  using Gm = Geom<T, D>;
+  float sc[2][G];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < Gm::kWords; ++j) a = dot_word<T>(q[g][j], r.k[i][j], a);
+      sc[i][g] = a;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc[i][g] = group8_sum(sc[i][g]) * scale_log2;
+  }
+  bool valid[2] = {true, true};
+  if constexpr (kMasked) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      valid[i] = (i * kGroups + grp) < n_valid;
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? sc[i][g] : -INFINITY;
+    }
+  }
+  bool raise = false;
+#pragma unroll
+  for (int g = 0; g < G; ++g) raise |= fmaxf(sc[0][g], sc[1][g]) > st.m[g] + kLazyMaxSlack;
+  if (raise) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(st.m[g], fmaxf(sc[0][g], sc[1][g]));
+      const float a = (st.m[g] == -INFINITY) ? 0.0f : fast_exp2(st.m[g] - mn);
+      st.l[g] *= a;
+#pragma unroll
+      for (int e = 0; e < Gm::kElems; ++e) st.acc[g][e] *= a;
+      st.m[g] = mn;
+    }
+  }
+  float p[2][G];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float e = fast_exp2(sc[i][g] - st.m[g]);
+      p[i][g] = (kMasked && !valid[i]) ? 0.0f : e;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) st.l[g] += p[0][g] + p[1][g];
+  float v0[Gm::kElems], v1[Gm::kElems];
+  widen<T, D>(r.v[0], v0);
+  widen<T, D>(r.v[1], v1);
+  if constexpr (kMasked) {
+    // select, not multiply: stale or NaN slots must not reach the accumulator
+#pragma unroll
+    for (int e = 0; e < Gm::kElems; ++e) {
+      v0[e] = valid[0] ? v0[e] : 0.0f;
+      v1[e] = valid[1] ? v1[e] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < Gm::kElems; ++e)
+      st.acc[g][e] = fmaf(p[1][g], v1[e], fmaf(p[0][g], v0[e], st.acc[g][e]));
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
+    int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
+    int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
+    float* __restrict__ out, float* __restrict__ lse) {
+  using Gm = Geom<T, D>;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int grp = lane / kLanesPerToken;
+  const int sub = lane % kLanesPerToken;
+
+  int n = ctx_lens[s];
+  const int cap = W * kBlockTokens;
+  if (n < 0 || n > cap) {
+    if (threadIdx.x == 0 && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+    n = n < 0 ? 0 : cap;
+  }
+  int nparts = 1;
+  int tok0 = 0, tok1 = n;
+  if (part_tokens > 0) {
+    nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
+    tok0 = part * part_tokens;
+    tok1 = min(n, tok0 + part_tokens);
+  }
+  if (part == static_cast<int>(gridDim.x) - 1 && nparts > static_cast<int>(gridDim.x) &&
+      threadIdx.x == 0 && kvh == 0)
+    PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
+  if (part >= nparts) return;
+
+  // Query rows of this KV head's group, this lane's dims, raw bits.
+  uint32_t qr[G][Gm::kWords];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const T* qrow = q + (static_cast<size_t>(s) * num_q_heads + kvh * G + g) * D;
+#pragma unroll
+    for (int c = 0; c < Gm::kChunks; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + c * Gm::kChunkStride +
+                                                      sub * Gm::kChunkElems);
+      qr[g][4 * c + 0] = w.x; qr[g][4 * c + 1] = w.y;
+      qr[g][4 * c + 2] = w.z; qr[g][4 * c + 3] = w.w;
+    }
+  }
+
+  GroupState<T, D, G> st;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = -INFINITY;
+    st.l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < Gm::kElems; ++e) st.acc[g][e] = 0.0f;
+  }
+
+  const int b_begin = tok0 / kBlockTokens;
+  const int nfull = tok1 / kBlockTokens - b_begin;  // blocks wholly inside [tok0, tok1)
+  const int tail = tok1 % kBlockTokens;             // valid tokens of a trailing partial block
+  const int nfull_w = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+
+  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
+  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
+  const T* kbase = kc + kvh * head_elems;
+  const T* vbase = vc + kvh * head_elems;
+  const int lane_off = grp * D + sub * Gm::kChunkElems;
+  const int32_t* trow = tables + static_cast<size_t>(s) * W;
+
+  // Block ids of this wave's full blocks, 64 at a time, one per lane.
+  int id_base = 0;
+  auto fetch_ids = [&](int base) -> int {
+    const int k = base + lane;
+    int id = 0;
+    bool bad = false;
+    if (k < nfull_w) {
+      id = trow[b_begin + wave + kWaves * k];
+      bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
+      id = bad ? 0 : id;
+    }
+    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+    return id;
+  };
+  int ids = fetch_ids(0);
+  auto block_of = [&](int k) -> int {
+    if (k - id_base >= kWave) {
+      id_base += kWave;
+      ids = fetch_ids(id_base);
+    }
+    return __builtin_amdgcn_readlane(ids, k - id_base);
+  };
+  auto tile_k = [&](int blk) { return kbase + static_cast<size_t>(blk) * block_elems; };
+  auto tile_v = [&](int blk) { return vbase + static_cast<size_t>(blk) * block_elems; };
+
+  TokenRegs<T, D> ra, rb;
+  int k = 0;
+  if (nfull_w > 0) {
+    const int b = block_of(0);
+    load_block<T, D>(ra, tile_k(b), tile_v(b), lane_off);
+  }
+  for (; k + 2 <= nfull_w; k += 2) {
+    const int b1 = block_of(k + 1);
+    load_block<T, D>(rb, tile_k(b1), tile_v(b1), lane_off);
+    process_block<T, D, G, false>(ra, qr, st, scale_log2, grp, kBlockTokens);
+    if (k + 2 < nfull_w) {
+      const int b2 = block_of(k + 2);
+      load_block<T, D>(ra, tile_k(b2), tile_v(b2), lane_off);
+    }
+    process_block<T, D, G, false>(rb, qr, st, scale_log2, grp, kBlockTokens);
+  }
+  if (k < nfull_w) process_block<T, D, G, false>(ra, qr, st, scale_log2, grp, kBlockTokens);
+
+  // The trailing partial block (only in the partition holding the sequence end)
+  // goes to the wave next in the interleave.
+  if (tail != 0 && wave == nfull % kWaves) {
+    int b = trow[b_begin + nfull];
+    if (static_cast<unsigned>(b) >= static_cast<unsigned>(num_blocks)) {
+      if (lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+      b = 0;
+    }
+    load_block<T, D>(ra, tile_k(b), tile_v(b), lane_off);
+    process_block<T, D, G, true>(ra, qr, st, scale_log2, grp, tail);
+  }
+
+  // Merge the 8 token groups of the wave (lanes with equal `sub` hold the same dims).
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = st.m[g];
+    mx = fmaxf(mx, __shfl_xor(mx, 8));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float a = (st.m[g] == -INFINITY) ? 0.0f : fast_exp2(st.m[g] - mx);
+    float l = st.l[g] * a;
+    l += __shfl_xor(l, 8);
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    st.l[g] = l;
+#pragma unroll
+    for (int e = 0; e < Gm::kElems; ++e) {
+      float x = st.acc[g][e] * a;
+      x += __shfl_xor(x, 8);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      st.acc[g][e] = x;
+    }
+    st.m[g] = mx;
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ float s_acc[kWaves][G][D];
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < Gm::kElems; ++e) s_acc[wave][g][lane_dim<T, D>(sub, e)] = st.acc[g][e];
+      if (sub == 0) {
+        s_m[wave][g] = st.m[g];
+        s_l[wave][g] = st.l[g];
+      }
+    }
+  }
+  __syncthreads();
+
+  const bool direct = (nparts == 1) && (out != nullptr);
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float a = (s_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][g] - M);
+      L = fmaf(s_l[w][g], a, L);
+      O = fmaf(s_acc[w][g][d], a, O);
+    }
+    const float o = L > 0.0f ? O / L : 0.0f;
+    const float ls = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    const int h = kvh * G + g;
+    const size_t sh = static_cast<size_t>(s) * num_q_heads + h;
+    if (direct) {
+      out[sh * D + d] = o;
+      if (lse != nullptr && d == 0) lse[sh] = ls;
+    } else {
+      part_out[(sh * max_parts + part) * D + d] = o;
+      if (d == 0) part_lse[sh * max_parts + part] = ls;
+    }
+  }
+}
+
+// Second pass: merge a (sequence, query head)'s partitions by log-sum-exp.
+__global__ __launch_bounds__(kWave) void lse_combine_kernel(
+    float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
+    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens, int cap,
+    int num_q_heads, int D, int part_tokens, int max_parts, int skip_single) {
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  int n = ctx_lens[s];
+  n = n < 0 ? 0 : min(n, cap);
+  int nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
+  nparts = min(nparts, max_parts);
+  if (skip_single && nparts == 1) return;
+  const size_t sh = static_cast<size_t>(s) * num_q_heads + h;
+  const float* pl = part_lse + sh * max_parts;
+  const float* po = part_out + sh * max_parts * D;
+  constexpr float kLog2e = 1.44269504088896340736f;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, pl[p]);
+  float den = 0.0f;
+  float num[2] = {0.0f, 0.0f};  // D <= 128 = 2 per lane
+  for (int p = 0; p < nparts; ++p) {
+    const float lp = pl[p];
+    const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
+    den += w;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int d = threadIdx.x + j * kWave;
+      if (d < D) num[j] = fmaf(w, po[p * D + d], num[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int d = threadIdx.x + j * kWave;
+    if (d < D) out[sh * D + d] = den > 0.0f ? num[j] / den : 0.0f;
+  }
+  if (lse != nullptr && threadIdx.x == 0) lse[sh] = den > 0.0f ? M + __logf(den) : -INFINITY;
+}
+
+using LaunchFn = void (*)(dim3, hipStream_t, const void*, const void*, const void*,
+                          const int32_t*, int, const int32_t*, int, int, int, float, int, int,
+                          float*, float*, float*, float*);
+
+template <typename T, int D, int G>
+void pass1_launch(dim3 grid, hipStream_t stream, const void* q, const void* kc, const void* vc,
+                  const int32_t* tables, int W, const int32_t* ctx, int hq, int hkv, int nb,
+                  float scale_log2, int part_tokens, int max_parts, float* part_out,
+                  float* part_lse, float* out, float* lse) {
+  hipLaunchKernelGGL((decode_pass1_kernel<T, D, G>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(kc),
+                     static_cast<const T*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
+                     part_tokens, max_parts, part_out, part_lse, out, lse);
+}
+
+template <typename T, int D>
+bool pick_group(int G, LaunchFn* fn) {
+  switch (G) {
+    case 1: *fn = pass1_launch<T, D, 1>; return true;
+    case 2: *fn = pass1_launch<T, D, 2>; return true;
+    case 3: *fn = pass1_launch<T, D, 3>; return true;
+    case 4: *fn = pass1_launch<T, D, 4>; return true;
+    case 5: *fn = pass1_launch<T, D, 5>; return true;
+    case 6: *fn = pass1_launch<T, D, 6>; return true;
+    case 7: *fn = pass1_launch<T, D, 7>; return true;
+    case 8: *fn = pass1_launch<T, D, 8>; return true;
+    default: return false;
+  }
+}
+
+int check_decode_args(const void* q, const void* kc, const void* vc, const int32_t* tables,
+                      int64_t bt_stride, const int32_t* ctx, int32_t batch, int32_t hq,
+                      int32_t hkv, int32_t D, int32_t bs, int32_t nb, int32_t max_ctx,
+                      int32_t part_tokens, int32_t dtype, LaunchFn* fn) {
+  if (!q || !kc || !vc || !tables || !ctx) return PKV_ERR_NULL;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || bs != kBlockTokens || nb <= 0 ||
+      max_ctx < 0 || bt_stride <= 0 || bt_stride > (1 << 26) || part_tokens < 0 ||
+      part_tokens % kBlockTokens != 0)
+    return PKV_ERR_SHAPE;
+  if (D != 64 && D != 128) return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_ctx) > bt_stride * kBlockTokens) return PKV_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc)) return PKV_ERR_ARG;
+  const int G = hq / hkv;
+  bool ok;
+  if (dtype == PKV_F32)
+    ok = D == 64 ? pick_group<float, 64>(G, fn) : pick_group<float, 128>(G, fn);
+  else
+    ok = D == 64 ? pick_group<uint16_t, 64>(G, fn) : pick_group<uint16_t, 128>(G, fn);
+  return ok ? PKV_OK : PKV_ERR_SHAPE;
+}
+
+int num_partitions(int32_t max_ctx, int32_t part_tokens) {
+  if (part_tokens <= 0) return 1;
+  return max_ctx > 0 ? (max_ctx + part_tokens - 1) / part_tokens : 1;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+float scale_to_log2(float scale) {
+  return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                             int32_t head_dim, int32_t max_context_len,
+                                             int32_t partition_size) {
+  const int np = num_partitions(max_context_len, partition_size);
+  if (partition_size <= 0 || np <= 1 || batch <= 0 || num_q_heads <= 0 || head_dim <= 0)
+    return 0;
+  const size_t rows = static_cast<size_t>(batch) * num_q_heads * np;
+  return align_up(rows * head_dim * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+extern "C" int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                int64_t bt_stride, const int32_t* context_lens, int32_t batch,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                                float scale, int32_t partition_size, void* workspace,
+                                size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+  LaunchFn fn = nullptr;
+  int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
+                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_context_len, partition_size, dtype, &fn);
+  if (st != PKV_OK) return st;
+  if (!out) return PKV_ERR_NULL;
+  if (batch == 0) return PKV_OK;
+  const int np = num_partitions(max_context_len, partition_size);
+  const size_t need =
+      pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  float* part_out = nullptr;
+  float* part_lse = nullptr;
+  if (need > 0) {
+    const size_t rows = static_cast<size_t>(batch) * num_q_heads * np;
+    part_out = static_cast<float*>(workspace);
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align_up(rows * head_dim * sizeof(float)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int tokens = partition_size > 0 && np > 1 ? partition_size : 0;
+  dim3 grid(np, num_kv_heads, batch);
+  fn(grid, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride), context_lens,
+     num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), tokens, np, part_out,
+     part_lse, out, lse);
+  if ((st = launch_status()) != PKV_OK) return st;
+  if (np > 1) {
+    hipLaunchKernelGGL(lse_combine_kernel, dim3(num_q_heads, batch), dim3(kWave), 0, s, out, lse,
+                       part_out, part_lse, context_lens,
+                       static_cast<int>(bt_stride) * kBlockTokens, num_q_heads, head_dim,
+                       partition_size, np, 1);
+    st = launch_status();
+  }
+  return st;
+}
+
+extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int64_t bt_stride,
+                                         const int32_t* context_lens, int32_t batch,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_context_len,
+                                         float scale, int32_t partition_size,
+                                         int32_t max_partitions, int32_t dtype,
+                                         pkv_stream_t stream) {
+  LaunchFn fn = nullptr;
+  int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
+                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_context_len, partition_size, dtype, &fn);
+  if (st != PKV_OK) return st;
+  if (!part_out || !part_lse) return PKV_ERR_NULL;
+  if (partition_size <= 0) return PKV_ERR_SHAPE;
+  const int np = num_partitions(max_context_len, partition_size);
+  if (max_partitions < np) return PKV_ERR_SHAPE;
+  if (batch == 0) return PKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 grid(np, num_kv_heads, batch);
+  fn(grid, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride), context_lens,
+     num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), partition_size,
+     max_partitions, part_out, part_lse, nullptr, nullptr);
+  return launch_status();
+}
+
+extern "C" int pkv_lse_combine(float* out, float* lse, const float* part_out,
+                               const float* part_lse, const int32_t* context_lens, int32_t batch,
+                               int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                               int32_t max_partitions, pkv_stream_t stream) {
+  if (!out || !part_out || !part_lse || !context_lens) return PKV_ERR_NULL;
+  if (batch < 0 || num_q_heads <= 0 || head_dim <= 0 || head_dim > 2 * kWave ||
+      partition_size <= 0 || max_partitions <= 0)
+    return PKV_ERR_SHAPE;
+  if (batch == 0) return PKV_OK;
+  // Lengths above max_partitions * partition_size are clamped to it.
+  const int64_t cap64 = static_cast<int64_t>(max_partitions) * partition_size;
+  const int cap = cap64 > (1 << 30) ? (1 << 30) : static_cast<int>(cap64);
+  hipLaunchKernelGGL(lse_combine_kernel, dim3(num_q_heads, batch), dim3(kWave), 0,
+                     static_cast<hipStream_t>(stream), out, lse, part_out, part_lse,
+                     context_lens, cap, num_q_heads, head_dim, partition_size, max_partitions, 0);
+  return launch_status();
+}

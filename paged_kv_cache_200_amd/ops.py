@@ -1,0 +1,220 @@
+"""Torch-tensor front end of libpkv: argument marshalling only.
+
+Every function checks the tensors' device, dtype, shape and contiguity, then
+passes raw device pointers and sizes to the C ABI, enqueued on torch's current
+HIP stream.  All computation happens in the library's kernels.
+
+bfloat16 data may be given as torch.bfloat16 or as torch.uint16/int16 bit
+patterns.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+BLOCK_SIZE = 16
+_BF16_TYPES = (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def _kv_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.PKV_F32
+    if t.dtype in _BF16_TYPES:
+        return _lib.PKV_BF16
+    raise TypeError(f"unsupported K/V dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _same_kind(a: torch.Tensor, b: torch.Tensor, what: str):
+    if _kv_code(a) != _kv_code(b):
+        raise TypeError(f"{what}: dtype {a.dtype} does not match {b.dtype}")
+
+
+def _gpu(t: torch.Tensor, what: str, dtype=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype} (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _cache_dims(k_cache: torch.Tensor):
+    if k_cache.dim() != 4 or k_cache.shape[2] != BLOCK_SIZE:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, 16, head_dim]")
+    nb, hkv, _, d = k_cache.shape
+    return nb, hkv, d
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, block_tables, start_pos, cu_new_tokens,
+              stream=None) -> None:
+    """Write k_new/v_new [T, Hkv, D] at positions start_pos[s] + i (explicit, never inferred)."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new")):
+        _gpu(t, n)
+    _same_kind(k_cache, v_cache, "v_cache")
+    _same_kind(k_cache, k_new, "k_new")
+    _same_kind(k_cache, v_new, "v_new")
+    nb, hkv, d = _cache_dims(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(start_pos, "start_pos", torch.int32)
+    _gpu(cu_new_tokens, "cu_new_tokens", torch.int32)
+    B = start_pos.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or cu_new_tokens.shape[0] != B + 1:
+        raise ValueError("block_tables [B, W], start_pos [B], cu_new_tokens [B + 1] expected")
+    _lib.call("pkv_kv_append", _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+              _ptr(block_tables), block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens),
+              B, k_new.shape[0], hkv, d, BLOCK_SIZE, nb, _kv_code(k_cache), _stream(stream))
+
+
+def decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size) -> int:
+    return int(_lib.lib().pkv_decode_workspace_bytes(batch, num_q_heads, head_dim,
+                                                     max_context_len, partition_size))
+
+
+def _decode_checks(q, k_cache, v_cache, block_tables, context_lens):
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _gpu(t, n)
+    _same_kind(k_cache, v_cache, "v_cache")
+    _same_kind(k_cache, q, "q")
+    nb, hkv, d = _cache_dims(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if q.dim() != 3 or q.shape[2] != d:
+        raise ValueError("q must be [batch, num_q_heads, head_dim]")
+    B, hq, _ = q.shape
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(context_lens, "context_lens", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables [B, W] and context_lens [B] expected")
+    return B, hq, hkv, d, nb
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
+                 partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
+                 stream=None):
+    """Decode attention of q [B, Hq, D] over the paged caches.
+
+    Returns (out float32 [B, Hq, D], lse float32 [B, Hq] or None).
+    max_context_len is a host-side upper bound of context_lens.
+    """
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    _gpu(out, "out", torch.float32)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+    need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.call("pkv_paged_decode", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+              _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d,
+              BLOCK_SIZE, nb, int(max_context_len), float(scale), int(partition_size),
+              _ptr(workspace), wbytes, _kv_code(k_cache), _stream(stream))
+    return out, lse
+
+
+def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                          partition_size, scale=None, max_partitions=None, part_out=None,
+                          part_lse=None, stream=None):
+    """First pass only: (part_out [B, Hq, NP, D], part_lse [B, Hq, NP]) float32."""
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if partition_size <= 0:
+        raise ValueError("partition_size must be positive")
+    np_ = max(1, -(-int(max_context_len) // int(partition_size)))
+    if max_partitions is None:
+        max_partitions = np_
+    if part_out is None:
+        part_out = torch.empty((B, hq, max_partitions, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((B, hq, max_partitions), dtype=torch.float32, device=q.device)
+    _gpu(part_out, "part_out", torch.float32)
+    _gpu(part_lse, "part_lse", torch.float32)
+    _lib.call("pkv_paged_decode_partials", _ptr(part_out), _ptr(part_lse), _ptr(q),
+              _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+              _ptr(context_lens), B, hq, hkv, d, BLOCK_SIZE, nb, int(max_context_len),
+              float(scale), int(partition_size), int(max_partitions), _kv_code(k_cache),
+              _stream(stream))
+    return part_out, part_lse
+
+
+def lse_combine(part_out, part_lse, context_lens, partition_size, out=None, lse=None,
+                want_lse=True, stream=None):
+    """Merge partitions by log-sum-exp: (out [B, Hq, D], lse [B, Hq])."""
+    _gpu(part_out, "part_out", torch.float32)
+    _gpu(part_lse, "part_lse", torch.float32)
+    _gpu(context_lens, "context_lens", torch.int32)
+    if part_out.dim() != 4 or part_lse.shape != part_out.shape[:3]:
+        raise ValueError("part_out [B, Hq, NP, D] and part_lse [B, Hq, NP] expected")
+    B, hq, np_, d = part_out.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=part_out.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=part_out.device)
+    _gpu(out, "out", torch.float32)
+    _lib.call("pkv_lse_combine", _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
+              _ptr(context_lens), B, hq, d, int(partition_size), np_, _stream(stream))
+    return out, lse
+
+
+def copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
+    """Copy-on-write block copy: block dst[i] := block src[i] in both caches.
+
+    Caches may be one layer [NB, Hkv, 16, D] or stacked layers [L, NB, Hkv, 16, D]
+    (every layer copied).
+    """
+    _gpu(k_cache, "k_cache")
+    _gpu(v_cache, "v_cache")
+    _same_kind(k_cache, v_cache, "v_cache")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if k_cache.dim() == 5:
+        layers = k_cache.shape[0]
+        layer_stride = k_cache.stride(0)
+        nb, hkv, d = _cache_dims(k_cache[0])
+    else:
+        layers, layer_stride = 1, 0
+        nb, hkv, d = _cache_dims(k_cache)
+    _gpu(src, "src", torch.int32)
+    _gpu(dst, "dst", torch.int32)
+    if src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be equal-length int32 vectors")
+    _lib.call("pkv_copy_blocks", _ptr(k_cache), _ptr(v_cache), _ptr(src), _ptr(dst),
+              src.shape[0], hkv, d, BLOCK_SIZE, nb, layers, layer_stride, _kv_code(k_cache),
+              _stream(stream))
+
+
+def device_error(stream=None) -> int:
+    """Synchronise the stream and return (and clear) the device error bits."""
+    flags = _lib._i32(0)
+    _lib.call("pkv_device_error", _stream(stream), _lib.ctypes.byref(flags))
+    return int(flags.value)
+
+
+def describe_device_error(flags: int) -> str:
+    return ", ".join(v for k, v in _lib.DEVICE_ERROR_BITS.items() if flags & k) or "none"

@@ -1,0 +1,59 @@
+"""The C-ABI library loads and exports every entry point the headers declare
+(no GPU needed; nothing here launches a kernel)."""
+
+import ctypes
+import os
+import re
+
+from libpkv_util import ROOT, ensure_built
+
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pkv.h", "pkv_block_manager.h")]
+DECL = re.compile(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(pkv_[a-z0-9_]+)\s*\(", re.M)
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        names += DECL.findall(open(h).read())
+    return sorted(set(names))
+
+
+def test_headers_declare_the_entry_points():
+    names = declared_functions()
+    for must in ("pkv_kv_append", "pkv_paged_decode", "pkv_paged_decode_partials",
+                 "pkv_lse_combine", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
+                 "pkv_device_error", "pkv_bm_create", "pkv_bm_prepare_write", "pkv_bm_fork"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ensure_built())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_binding_covers_every_declared_symbol():
+    ensure_built()
+    from paged_kv_cache_200_amd import _lib
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_host_only_calls():
+    ensure_built()
+    from paged_kv_cache_200_amd import _lib
+    lib = _lib.lib()
+    assert lib.pkv_version() == 100
+    assert lib.pkv_status_string(0) == b"ok"
+    assert lib.pkv_status_string(-3) == b"unsupported size or shape"
+    # workspace sizing is pure host arithmetic
+    assert lib.pkv_decode_workspace_bytes(4, 32, 128, 32768, 0) == 0
+    assert lib.pkv_decode_workspace_bytes(4, 32, 128, 512, 512) == 0
+    ws = lib.pkv_decode_workspace_bytes(4, 32, 128, 32768, 512)
+    assert ws >= 4 * 32 * 64 * (128 + 1) * 4
+    # argument errors are reported before any launch
+    st = lib.pkv_paged_decode(None, None, None, None, None, None, 1, None, 1, 8, 2, 64, 16, 4,
+                              16, 1.0, 0, None, 0, 0, None)
+    assert st == -1
+    st = lib.pkv_kv_append(None, None, None, None, None, 1, None, None, 1, 0, 1, 64, 16, 4, 0,
+                           None)
+    assert st == 0  # nothing to append

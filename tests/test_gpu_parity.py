@@ -1,0 +1,289 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Indexing (append, block copy, the one-hot gather probe,
+batched-vs-alone, forks) must be bit-exact; attention values within 2e-3
+max-abs for fp32 caches and 1e-2 for bf16 caches (fp32 accumulation)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged_attention as pa
+from gpu_util import (TOL, DeviceCase, assert_no_device_error, assert_parity, dev, host_bits,
+                      oracle_decode, run_decode, say)
+from libpkv_util import ensure_built
+from workloads import bf16_bits, build_case, config_case, fork_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ensure_built()
+    import paged_kv_cache_200_amd  # noqa: F401
+
+
+def _ops():
+    from paged_kv_cache_200_amd import ops
+    return ops
+
+
+# --------------------------------------------------------------------------------------
+# KV append and block copy: bit-exact
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype,hkv,d", [("f32", 12, 64), ("bf16", 2, 64), ("bf16", 8, 128),
+                                            ("f32", 4, 128)])
+def test_append_bitexact(kv_dtype, hkv, d):
+    say(f"append {kv_dtype} hkv={hkv} d={d}")
+    rng = np.random.default_rng(hkv * 1000 + d)
+    case = build_case("append", [40, 100, 1, 77, 200], hkv, hkv, d, kv_dtype, seed=d + hkv)
+    B = case.batch
+    # a prefill-like write of several tokens per sequence at explicit starts, some
+    # crossing block boundaries, one empty, then a one-token decode write
+    for starts, counts in (([0, 13, 0, 60, 150], [16, 40, 1, 0, 33]),
+                           (list(case.context_lens - 1), [1] * B)):
+        starts = np.array(starts, np.int32)
+        cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        x = rng.standard_normal((int(cu[-1]), hkv, d)).astype(np.float32)
+        y = rng.standard_normal((int(cu[-1]), hkv, d)).astype(np.float32)
+        if kv_dtype == "bf16":
+            x, y = bf16_bits(x), bf16_bits(y)
+        kd, vd = dev(case.k_pool[0]), dev(case.v_pool[0])
+        _ops().kv_append(kd, vd, dev(x), dev(y), dev(case.block_tables), dev(starts), dev(cu))
+        want_k, want_v = pa.kv_append(case.k_pool[0], case.v_pool[0], x, y, case.block_tables,
+                                      starts, cu)
+        assert host_bits(kd, kv_dtype).tobytes() == want_k.tobytes()
+        assert host_bits(vd, kv_dtype).tobytes() == want_v.tobytes()
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
+def test_copy_blocks_bitexact(kv_dtype):
+    case = build_case("copy", [64, 64, 64], 4, 4, 128, kv_dtype, seed=3, layers=3)
+    k = dev(case.k_pool)
+    v = dev(case.v_pool)
+    src, dst = [0, 5, 2], [7, 1, 9]
+    _ops().copy_blocks(k, v, dev(np.array(src, np.int32)), dev(np.array(dst, np.int32)))
+    for layer in range(3):
+        wk, wv = pa.copy_blocks(case.k_pool[layer], case.v_pool[layer], src, dst)
+        assert host_bits(k[layer], kv_dtype).tobytes() == wk.tobytes()
+        assert host_bits(v[layer], kv_dtype).tobytes() == wv.tobytes()
+    # one layer at a time
+    k1 = dev(case.k_pool[0])
+    v1 = dev(case.v_pool[0])
+    _ops().copy_blocks(k1, v1, dev(np.array(src, np.int32)), dev(np.array(dst, np.int32)))
+    wk, wv = pa.copy_blocks(case.k_pool[0], case.v_pool[0], src, dst)
+    assert host_bits(k1, kv_dtype).tobytes() == wk.tobytes()
+    assert_no_device_error()
+
+
+# --------------------------------------------------------------------------------------
+# Decode parity on the workload configs
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("P", [0, 16, 64, 512])
+def test_decode_tiny(seed, P):
+    say(f"tiny seed={seed} P={P}")
+    case = config_case("tiny", seed)
+    assert_parity(run_decode(DeviceCase(case), P), oracle_decode(case), "f32", f"tiny s{seed}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_qwen_gqa(seed):
+    layers = 24 if seed == 0 else 3
+    say(f"qwen_gqa seed={seed} layers={layers}")
+    case = config_case("qwen_gqa", seed, layers=layers)
+    for layer in range(layers):
+        for P in ((0, 256) if layer % 6 == 0 else (256,)):
+            assert_parity(run_decode(DeviceCase(case, layer), P), oracle_decode(case, layer),
+                          "bf16", f"qwen s{seed} L{layer} P{P}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_high_concurrency(seed):
+    say(f"high_concurrency seed={seed}")
+    case = config_case("high_concurrency", seed)
+    want = oracle_decode(case)
+    dc = DeviceCase(case)
+    for P in (512,) if seed else (512, 256, 0):
+        assert_parity(run_decode(dc, P), want, "bf16", f"C4 s{seed} P{P}")
+    assert_no_device_error()
+
+
+def test_decode_prefix_fork():
+    say("prefix_fork")
+    case = config_case("prefix_fork", 0)
+    assert_parity(run_decode(DeviceCase(case), 512), oracle_decode(case), "bf16", "C5a")
+    assert_no_device_error()
+
+
+def test_decode_long_context():
+    say("long_context")
+    case = config_case("long_context", 0)
+    assert_parity(run_decode(DeviceCase(case), 512), oracle_decode(case), "bf16", "C5b P512")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P", [16, 512])
+def test_partials_and_combine(kv_dtype, P):
+    case = build_case("parts", [0, 1, 15, 16, 17, 511, 512, 513, 1500], 8, 2, 128, kv_dtype, 5)
+    dc = DeviceCase(case)
+    ops = _ops()
+    po, pl = ops.paged_decode_partials(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx, P,
+                                       scale=float(case.scale), max_partitions=None)
+    wpo, wpl = pa.decode_partitions(case.q[0], case.k_pool[0], case.v_pool[0],
+                                    case.block_tables, case.context_lens, case.scale, kv_dtype, P)
+    # entries past a sequence's last partition are not written: compare the live ones
+    live = np.zeros(wpl.shape, bool)
+    for s, n in enumerate(case.context_lens.tolist()):
+        live[s, :, :max(1, -(-n // P))] = True
+    gpo, gpl = po.cpu().numpy(), pl.cpu().numpy()
+    assert_parity((gpo[live], gpl[live]), (wpo[live], wpl[live]), kv_dtype, f"partials P{P}")
+    o, l = ops.lse_combine(po, pl, dc.ctx, P)
+    assert_parity((o.cpu().numpy(), l.cpu().numpy()), pa.combine_partitions(wpo, wpl), kv_dtype,
+                  f"combine P{P}")
+    assert_parity((o.cpu().numpy(), l.cpu().numpy()), oracle_decode(case), kv_dtype, "vs unsplit")
+    assert_no_device_error()
+
+
+# --------------------------------------------------------------------------------------
+# Edge cases
+# --------------------------------------------------------------------------------------
+
+BOUNDARY_LENS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023,
+                 1024, 1025, 2047]
+
+
+@pytest.mark.parametrize("kv_dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f32", 12, 12, 64),
+                                               ("bf16", 14, 2, 64), ("bf16", 8, 8, 128),
+                                               ("f32", 16, 2, 128), ("bf16", 5, 1, 64)])
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_block_and_partition_boundaries(kv_dtype, hq, hkv, d, P):
+    case = build_case("bounds", BOUNDARY_LENS, hq, hkv, d, kv_dtype, seed=hq + d + P)
+    assert_parity(run_decode(DeviceCase(case), P), oracle_decode(case), kv_dtype,
+                  f"bounds {kv_dtype} G{hq // hkv} D{d} P{P}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 32])
+def test_empty_contexts(P):
+    case = build_case("empty", [0, 5, 0, 40, 0], 8, 2, 64, "bf16", seed=1)
+    o, l = run_decode(DeviceCase(case), P)
+    assert np.all(o[[0, 2, 4]] == 0) and np.all(l[[0, 2, 4]] == -np.inf)
+    assert_parity((o, l), oracle_decode(case), "bf16", f"empty P{P}")
+    allzero = build_case("allempty", [0, 0], 4, 4, 64, "f32", seed=2)
+    o, l = run_decode(DeviceCase(allzero), P)
+    assert np.all(o == 0) and np.all(l == -np.inf)
+    assert_no_device_error()
+
+
+def test_max_context_len_above_true_max():
+    case = build_case("slack", [100, 700, 33], 8, 2, 128, "bf16", seed=4, table_width=200)
+    want = oracle_decode(case)
+    dc = DeviceCase(case)
+    for max_ctx in (700, 701, 1024, 3200):
+        assert_parity(run_decode(dc, 64, max_ctx=max_ctx), want, "bf16", f"max_ctx {max_ctx}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("q_scale", [8.0, 30.0])
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
+def test_softmax_stability(q_scale, kv_dtype):
+    case = build_case("stable", [3, 90, 600, 1300], 16, 4, 128 if kv_dtype == "bf16" else 64,
+                      kv_dtype, seed=9, q_scale=q_scale)
+    want = oracle_decode(case)
+    dc = DeviceCase(case)
+    for P in (0, 128):
+        assert_parity(run_decode(dc, P), want, kv_dtype, f"q x{q_scale} P{P}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("kv_dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("P", [0, 64])
+def test_one_hot_gather_probe_bitwise(kv_dtype, d, P):
+    """One token per sequence scores >= 100 above all others: out must be that
+    token's V row exactly, which makes the gather's indexing bit-checkable."""
+    lens = [1, 17, 130, 700]
+    case = build_case("probe", lens, 4, 2, d, kv_dtype, seed=d + P)
+    rng = np.random.default_rng(7)
+    kp = case.k_pool[0].copy()
+    q = np.zeros_like(case.q[0])
+    one = np.float32(1.0) if kv_dtype == "f32" else bf16_bits(np.float32(1.0))
+    big = np.float32(160.0) if kv_dtype == "f32" else bf16_bits(np.float32(160.0))
+    small = np.float32(0.0) if kv_dtype == "f32" else bf16_bits(np.float32(0.0))
+    q[:, :, 0] = one
+    hot = []
+    for s, n in enumerate(lens):
+        t = int(rng.integers(n))
+        hot.append(t)
+        for tt in range(n):
+            blk, slot = case.block_tables[s, tt // 16], tt % 16
+            kp[blk, :, slot, 0] = big if tt == t else small
+    case.k_pool = kp[None]
+    case.q = q[None]
+    case.scale = np.float32(1.0)
+    o, l = run_decode(DeviceCase(case), P)
+    vals = pa.widen(case.v_pool[0], kv_dtype)
+    G = 2
+    for s, t in enumerate(hot):
+        blk, slot = case.block_tables[s, t // 16], t % 16
+        for h in range(4):
+            row = vals[blk, h // G, slot].astype(np.float32)
+            assert o[s, h].astype(np.float32).tobytes() == row.tobytes(), (s, h)
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_batched_equals_alone_bitwise(P):
+    """A sequence decoded in a batch or alone gives bit-identical out and lse
+    (no attention leaks across sequence boundaries)."""
+    case = config_case("high_concurrency", 1, max_batch=24)
+    dc = DeviceCase(case)
+    ob, lb = run_decode(dc, P)
+    ops = _ops()
+    for s in range(case.batch):
+        o, l = ops.paged_decode(dc.q[s:s + 1], dc.k, dc.v, dc.tables[s:s + 1].contiguous(),
+                                dc.ctx[s:s + 1].contiguous(), int(case.context_lens[s]),
+                                scale=float(case.scale), partition_size=P)
+        assert o.cpu().numpy().tobytes() == ob[s:s + 1].astype(np.float32).tobytes(), s
+        assert l.cpu().numpy().tobytes() == lb[s:s + 1].astype(np.float32).tobytes(), s
+    assert_no_device_error()
+
+
+def test_forks_bitwise_identical():
+    case = fork_case("forks", [2048, 40, 500], 4, [[0] * 4] * 3, 32, 8, 128, "bf16", seed=3)
+    q = case.q[0].copy()
+    for s in range(case.batch):
+        q[s] = q[case.fork_parent[s] * 4]
+    case.q = q[None]
+    for P in (0, 512):
+        o, l = run_decode(DeviceCase(case), P)
+        for s in range(case.batch):
+            f0 = case.fork_parent[s] * 4
+            assert o[s].tobytes() == o[f0].tobytes() and l[s].tobytes() == l[f0].tobytes()
+        assert_parity((o, l), oracle_decode(case), "bf16", f"forks P{P}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("fill", ["inf", "huge"])
+def test_stale_slots_never_leak(fill):
+    """Unowned slots holding inf or huge values instead of NaN change nothing."""
+    case = build_case("stale", [5, 16, 33, 250], 8, 2, 64, "f32", seed=11)
+    ref = run_decode(DeviceCase(case), 64)
+    kp, vp = case.k_pool.copy(), case.v_pool.copy()
+    val = np.float32(np.inf) if fill == "inf" else np.float32(3e38)
+    nan_k = np.isnan(kp)
+    kp[nan_k] = val
+    vp[np.isnan(vp)] = -val
+    case.k_pool, case.v_pool = kp, vp
+    got = run_decode(DeviceCase(case), 64)
+    assert got[0].tobytes() == ref[0].tobytes() and got[1].tobytes() == ref[1].tobytes()
+    assert_parity(got, oracle_decode(case), "f32", f"stale {fill}")
+    assert_no_device_error()
