@@ -38,8 +38,6 @@ namespace {
 
 constexpr int kLanesPerToken = 8;
 constexpr int kGroups = kWave / kLanesPerToken;  // token groups per wave
-constexpr int kWaves = 4;                        // wavefronts per workgroup
-constexpr int kThreads = kWaves * kWave;
 constexpr float kLazyMaxSlack = 8.0f;            // log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -201,26 +199,43 @@ __device__ __forceinline__ void process_block(const TokenRegs<T, D>& r,
   }
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
+// Grid layouts of the first pass.
+//   kOrderPartMinor: x = partition, y = KV-head group, z = sequence.
+//   kOrderPartMajorReversed: x = KV-head group, y = sequence, z = partition counted from
+//     the last one, so the later partitions of the longest sequences are dispatched first
+//     and every sequence's first (often shortest) partition last.
+constexpr int kOrderPartMinor = 0;
+constexpr int kOrderPartMajorReversed = 1;
+
+// NW wavefronts per workgroup.  NW > 1: the waves share one (sequence, KV head,
+// partition) and take its blocks round-robin, merging through LDS at the end.  NW == 1:
+// one wave owns the unit and writes its result straight from registers.
+// DEPTH: 16-token blocks whose loads are in flight per wave (1 being processed,
+// DEPTH - 1 prefetched).
+template <typename T, int D, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
     int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
     int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, int order) {
   using Gm = Geom<T, D>;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int part, kvh, s, nx_parts;
+  if (order == kOrderPartMinor) {
+    part = blockIdx.x; kvh = blockIdx.y; s = blockIdx.z; nx_parts = gridDim.x;
+  } else {
+    kvh = blockIdx.x; s = blockIdx.y; part = gridDim.z - 1 - blockIdx.z; nx_parts = gridDim.z;
+  }
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int grp = lane / kLanesPerToken;
   const int sub = lane % kLanesPerToken;
+  const bool leader = threadIdx.x == 0;
 
   int n = ctx_lens[s];
   const int cap = W * kBlockTokens;
   if (n < 0 || n > cap) {
-    if (threadIdx.x == 0 && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+    if (leader && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
     n = n < 0 ? 0 : cap;
   }
   int nparts = 1;
@@ -230,8 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
     tok0 = part * part_tokens;
     tok1 = min(n, tok0 + part_tokens);
   }
-  if (part == static_cast<int>(gridDim.x) - 1 && nparts > static_cast<int>(gridDim.x) &&
-      threadIdx.x == 0 && kvh == 0)
+  if (part == nx_parts - 1 && nparts > nx_parts && leader && kvh == 0)
     PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
   if (part >= nparts) return;
 
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
   const int b_begin = tok0 / kBlockTokens;
   const int nfull = tok1 / kBlockTokens - b_begin;  // blocks wholly inside [tok0, tok1)
   const int tail = tok1 % kBlockTokens;             // valid tokens of a trailing partial block
-  const int nfull_w = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+  const int nfull_w = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
 
   const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
   const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
@@ -277,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
     int id = 0;
     bool bad = false;
     if (k < nfull_w) {
-      id = trow[b_begin + wave + kWaves * k];
+      id = trow[b_begin + wave + NW * k];
       bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
       id = bad ? 0 : id;
     }
@@ -285,44 +299,43 @@ __global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
     return id;
   };
   int ids = fetch_ids(0);
-  auto block_of = [&](int k) -> int {
+  auto block_of = [&](int k) -> int {  // called with k = 0, 1, 2, ... in order
     if (k - id_base >= kWave) {
       id_base += kWave;
       ids = fetch_ids(id_base);
     }
     return __builtin_amdgcn_readlane(ids, k - id_base);
   };
-  auto tile_k = [&](int blk) { return kbase + static_cast<size_t>(blk) * block_elems; };
-  auto tile_v = [&](int blk) { return vbase + static_cast<size_t>(blk) * block_elems; };
+  auto load = [&](TokenRegs<T, D>& r, int blk) {
+    load_block<T, D>(r, kbase + static_cast<size_t>(blk) * block_elems,
+                     vbase + static_cast<size_t>(blk) * block_elems, lane_off);
+  };
 
-  TokenRegs<T, D> ra, rb;
-  int k = 0;
-  if (nfull_w > 0) {
-    const int b = block_of(0);
-    load_block<T, D>(ra, tile_k(b), tile_v(b), lane_off);
-  }
-  for (; k + 2 <= nfull_w; k += 2) {
-    const int b1 = block_of(k + 1);
-    load_block<T, D>(rb, tile_k(b1), tile_v(b1), lane_off);
-    process_block<T, D, G, false>(ra, qr, st, scale_log2, grp, kBlockTokens);
-    if (k + 2 < nfull_w) {
-      const int b2 = block_of(k + 2);
-      load_block<T, D>(ra, tile_k(b2), tile_v(b2), lane_off);
+  TokenRegs<T, D> rr[DEPTH];
+#pragma unroll
+  for (int j = 0; j + 1 < DEPTH; ++j)
+    if (j < nfull_w) load(rr[j], block_of(j));
+  for (int k = 0; k < nfull_w; k += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      if (k + j < nfull_w) {
+        const int ahead = k + j + DEPTH - 1;
+        if (ahead < nfull_w) load(rr[(j + DEPTH - 1) % DEPTH], block_of(ahead));
+        process_block<T, D, G, false>(rr[j], qr, st, scale_log2, grp, kBlockTokens);
+      }
     }
-    process_block<T, D, G, false>(rb, qr, st, scale_log2, grp, kBlockTokens);
   }
-  if (k < nfull_w) process_block<T, D, G, false>(ra, qr, st, scale_log2, grp, kBlockTokens);
 
   // The trailing partial block (only in the partition holding the sequence end)
-  // goes to the wave next in the interleave.
-  if (tail != 0 && wave == nfull % kWaves) {
+  // goes to the wave next in the round-robin.
+  if (tail != 0 && wave == nfull % NW) {
     int b = trow[b_begin + nfull];
     if (static_cast<unsigned>(b) >= static_cast<unsigned>(num_blocks)) {
       if (lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
       b = 0;
     }
-    load_block<T, D>(ra, tile_k(b), tile_v(b), lane_off);
-    process_block<T, D, G, true>(ra, qr, st, scale_log2, grp, tail);
+    load(rr[0], b);
+    process_block<T, D, G, true>(rr[0], qr, st, scale_log2, grp, tail);
   }
 
   // Merge the 8 token groups of the wave (lanes with equal `sub` hold the same dims).
@@ -349,115 +362,213 @@ __global__ __launch_bounds__(kThreads) void decode_pass1_kernel(
     st.m[g] = mx;
   }
 
-  // Merge the waves through LDS.
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_acc[kWaves][G][D];
-  if (grp == 0) {
+  const bool direct = (nparts == 1) && (out != nullptr);
+  if constexpr (NW == 1) {
+    // Lanes of token group 0 hold the totals for their dims: write them.
+    if (grp == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < G; ++g) {
+        const float L = st.l[g];
+        const float ls = L > 0.0f ? (st.m[g] + __log2f(L)) * kLn2 : -INFINITY;
+        const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
+        float* dst = direct ? out + sh * D : part_out + (sh * max_parts + part) * D;
 #pragma unroll
-      for (int e = 0; e < Gm::kElems; ++e) s_acc[wave][g][lane_dim<T, D>(sub, e)] = st.acc[g][e];
-      if (sub == 0) {
-        s_m[wave][g] = st.m[g];
-        s_l[wave][g] = st.l[g];
+        for (int e = 0; e < Gm::kElems; e += 4) {
+          float4 v;
+          v.x = L > 0.0f ? st.acc[g][e + 0] / L : 0.0f;
+          v.y = L > 0.0f ? st.acc[g][e + 1] / L : 0.0f;
+          v.z = L > 0.0f ? st.acc[g][e + 2] / L : 0.0f;
+          v.w = L > 0.0f ? st.acc[g][e + 3] / L : 0.0f;
+          *reinterpret_cast<float4*>(dst + lane_dim<T, D>(sub, e)) = v;
+        }
+        if (sub == 0) {
+          if (direct) {
+            if (lse != nullptr) lse[sh] = ls;
+          } else {
+            part_lse[sh * max_parts + part] = ls;
+          }
+        }
       }
     }
-  }
-  __syncthreads();
-
-  const bool direct = (nparts == 1) && (out != nullptr);
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
+  } else {
+    // Merge the waves through LDS.
+    __shared__ float s_m[NW][G];
+    __shared__ float s_l[NW][G];
+    __shared__ float s_acc[NW][G][D];
+    if (grp == 0) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float L = 0.0f, O = 0.0f;
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float a = (s_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][g] - M);
-      L = fmaf(s_l[w][g], a, L);
-      O = fmaf(s_acc[w][g][d], a, O);
+        for (int e = 0; e < Gm::kElems; ++e)
+          s_acc[wave][g][lane_dim<T, D>(sub, e)] = st.acc[g][e];
+        if (sub == 0) {
+          s_m[wave][g] = st.m[g];
+          s_l[wave][g] = st.l[g];
+        }
+      }
     }
-    const float o = L > 0.0f ? O / L : 0.0f;
-    const float ls = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    const int h = kvh * G + g;
-    const size_t sh = static_cast<size_t>(s) * num_q_heads + h;
-    if (direct) {
-      out[sh * D + d] = o;
-      if (lse != nullptr && d == 0) lse[sh] = ls;
-    } else {
-      part_out[(sh * max_parts + part) * D + d] = o;
-      if (d == 0) part_lse[sh * max_parts + part] = ls;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+      const int g = idx / D;
+      const int d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float a = (s_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][g] - M);
+        L = fmaf(s_l[w][g], a, L);
+        O = fmaf(s_acc[w][g][d], a, O);
+      }
+      const float o = L > 0.0f ? O / L : 0.0f;
+      const float ls = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
+      if (direct) {
+        out[sh * D + d] = o;
+        if (lse != nullptr && d == 0) lse[sh] = ls;
+      } else {
+        part_out[(sh * max_parts + part) * D + d] = o;
+        if (d == 0) part_lse[sh * max_parts + part] = ls;
+      }
     }
   }
 }
 
-// Second pass: merge a (sequence, query head)'s partitions by log-sum-exp.
-__global__ __launch_bounds__(kWave) void lse_combine_kernel(
+// Second pass: merge a (sequence, query head)'s partitions by log-sum-exp.  One
+// wavefront per (sequence, query head), four per workgroup.  Lane p holds partition p's
+// log-sum-exp (64 partitions per round), so the max and the weight sum are wave
+// reductions; the weighted sum of the partial outputs then streams the partitions with
+// every lane owning D/64 output dims, four partitions per step.
+constexpr int kCombineWaves = 4;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
     float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
-    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens, int cap,
-    int num_q_heads, int D, int part_tokens, int max_parts, int skip_single) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
+    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens, int batch, int cap,
+    int num_q_heads, int part_tokens, int max_parts, int skip_single) {
+  constexpr int kPer = D / kWave;  // output dims per lane
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const int row = blockIdx.x * kCombineWaves + threadIdx.x / kWave;  // (s, h) flattened
+  const int lane = threadIdx.x % kWave;
+  if (row >= batch * num_q_heads) return;
+  const int s = row / num_q_heads;
   int n = ctx_lens[s];
   n = n < 0 ? 0 : min(n, cap);
   int nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
   nparts = min(nparts, max_parts);
   if (skip_single && nparts == 1) return;
-  const size_t sh = static_cast<size_t>(s) * num_q_heads + h;
+  const size_t sh = static_cast<size_t>(row);
   const float* pl = part_lse + sh * max_parts;
   const float* po = part_out + sh * max_parts * D;
-  constexpr float kLog2e = 1.44269504088896340736f;
+
   float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, pl[p]);
-  float den = 0.0f;
-  float num[2] = {0.0f, 0.0f};  // D <= 128 = 2 per lane
-  for (int p = 0; p < nparts; ++p) {
-    const float lp = pl[p];
-    const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
-    den += w;
+  for (int p0 = 0; p0 < nparts; p0 += kWave)
+    M = fmaxf(M, wave_max(p0 + lane < nparts ? pl[p0 + lane] : -INFINITY));
+  float acc[kPer];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = threadIdx.x + j * kWave;
-      if (d < D) num[j] = fmaf(w, po[p * D + d], num[j]);
+  for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
+  float den = 0.0f;
+  for (int p0 = 0; p0 < nparts; p0 += kWave) {
+    const int cnt = min(kWave, nparts - p0);
+    const float lp = lane < cnt ? pl[p0 + lane] : -INFINITY;
+    const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
+    den += wave_sum(w);
+    int p = 0;
+    for (; p + 4 <= cnt; p += 4) {
+      float wp[4];
+      float x[4][kPer];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wp[u] = __shfl(w, p + u);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) x[u][j] = po[(p0 + p + u) * D + j * kWave + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp[u], x[u][j], acc[j]);
+    }
+    for (; p < cnt; ++p) {
+      const float wp = __shfl(w, p);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp, po[(p0 + p) * D + j * kWave + lane], acc[j]);
     }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int d = threadIdx.x + j * kWave;
-    if (d < D) out[sh * D + d] = den > 0.0f ? num[j] / den : 0.0f;
-  }
-  if (lse != nullptr && threadIdx.x == 0) lse[sh] = den > 0.0f ? M + __logf(den) : -INFINITY;
+  for (int j = 0; j < kPer; ++j) out[sh * D + j * kWave + lane] = den > 0.0f ? acc[j] / den : 0.0f;
+  if (lse != nullptr && lane == 0) lse[sh] = den > 0.0f ? M + __logf(den) : -INFINITY;
 }
 
-using LaunchFn = void (*)(dim3, hipStream_t, const void*, const void*, const void*,
+void combine_launch(hipStream_t stream, float* out, float* lse, const float* part_out,
+                    const float* part_lse, const int32_t* ctx, int batch, int cap, int hq, int D,
+                    int part_tokens, int max_parts, int skip_single) {
+  const int rows = batch * hq;
+  const dim3 grid((rows + kCombineWaves - 1) / kCombineWaves);
+  if (D == 64)
+    hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineWaves * kWave), 0, stream, out,
+                       lse, part_out, part_lse, ctx, batch, cap, hq, part_tokens, max_parts,
+                       skip_single);
+  else
+    hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineWaves * kWave), 0, stream,
+                       out, lse, part_out, part_lse, ctx, batch, cap, hq, part_tokens, max_parts,
+                       skip_single);
+}
+
+using LaunchFn = void (*)(int, int, int, hipStream_t, const void*, const void*, const void*,
                           const int32_t*, int, const int32_t*, int, int, int, float, int, int,
                           float*, float*, float*, float*);
 
-template <typename T, int D, int G>
-void pass1_launch(dim3 grid, hipStream_t stream, const void* q, const void* kc, const void* vc,
-                  const int32_t* tables, int W, const int32_t* ctx, int hq, int hkv, int nb,
-                  float scale_log2, int part_tokens, int max_parts, float* part_out,
-                  float* part_lse, float* out, float* lse) {
-  hipLaunchKernelGGL((decode_pass1_kernel<T, D, G>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(kc),
+// Grid for `np` partitions: see kOrder*.
+template <int NW, int DEPTH, int kOrder, typename T, int D, int G>
+void pass1_launch(int np, int num_kv_heads, int batch, hipStream_t stream, const void* q,
+                  const void* kc, const void* vc, const int32_t* tables, int W,
+                  const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
+                  int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
+                  float* lse) {
+  const dim3 grid = kOrder == kOrderPartMinor ? dim3(np, num_kv_heads, batch)
+                                              : dim3(num_kv_heads, batch, np);
+  hipLaunchKernelGGL((decode_pass1_kernel<T, D, G, NW, DEPTH>), grid, dim3(NW * kWave), 0,
+                     stream, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
-                     part_tokens, max_parts, part_out, part_lse, out, lse);
+                     part_tokens, max_parts, part_out, part_lse, out, lse, kOrder);
+}
+
+// The configuration the library ships: four waves share a (sequence, KV head,
+// partition), two blocks in flight per wave, later partitions dispatched first.
+template <typename T, int D, int G>
+void pass1_default(int np, int num_kv_heads, int batch, hipStream_t stream, const void* q,
+                   const void* kc, const void* vc, const int32_t* tables, int W,
+                   const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
+                   int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
+                   float* lse) {
+  pass1_launch<4, 2, kOrderPartMajorReversed, T, D, G>(
+      np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx, hq, hkv, nb, scale_log2,
+      part_tokens, max_parts, part_out, part_lse, out, lse);
 }
 
 template <typename T, int D>
 bool pick_group(int G, LaunchFn* fn) {
   switch (G) {
-    case 1: *fn = pass1_launch<T, D, 1>; return true;
-    case 2: *fn = pass1_launch<T, D, 2>; return true;
-    case 3: *fn = pass1_launch<T, D, 3>; return true;
-    case 4: *fn = pass1_launch<T, D, 4>; return true;
-    case 5: *fn = pass1_launch<T, D, 5>; return true;
-    case 6: *fn = pass1_launch<T, D, 6>; return true;
-    case 7: *fn = pass1_launch<T, D, 7>; return true;
-    case 8: *fn = pass1_launch<T, D, 8>; return true;
+    case 1: *fn = pass1_default<T, D, 1>; return true;
+    case 2: *fn = pass1_default<T, D, 2>; return true;
+    case 3: *fn = pass1_default<T, D, 3>; return true;
+    case 4: *fn = pass1_default<T, D, 4>; return true;
+    case 5: *fn = pass1_default<T, D, 5>; return true;
+    case 6: *fn = pass1_default<T, D, 6>; return true;
+    case 7: *fn = pass1_default<T, D, 7>; return true;
+    case 8: *fn = pass1_default<T, D, 8>; return true;
     default: return false;
   }
 }
@@ -539,16 +650,14 @@ extern "C" int pkv_paged_decode(float* out, float* lse, const void* q, const voi
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int tokens = partition_size > 0 && np > 1 ? partition_size : 0;
-  dim3 grid(np, num_kv_heads, batch);
-  fn(grid, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride), context_lens,
-     num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), tokens, np, part_out,
-     part_lse, out, lse);
+  fn(np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride),
+     context_lens, num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), tokens, np,
+     part_out, part_lse, out, lse);
   if ((st = launch_status()) != PKV_OK) return st;
   if (np > 1) {
-    hipLaunchKernelGGL(lse_combine_kernel, dim3(num_q_heads, batch), dim3(kWave), 0, s, out, lse,
-                       part_out, part_lse, context_lens,
-                       static_cast<int>(bt_stride) * kBlockTokens, num_q_heads, head_dim,
-                       partition_size, np, 1);
+    combine_launch(s, out, lse, part_out, part_lse, context_lens, batch,
+                   static_cast<int>(bt_stride) * kBlockTokens, num_q_heads, head_dim,
+                   partition_size, np, 1);
     st = launch_status();
   }
   return st;
@@ -575,9 +684,8 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
   if (max_partitions < np) return PKV_ERR_SHAPE;
   if (batch == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(np, num_kv_heads, batch);
-  fn(grid, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride), context_lens,
-     num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), partition_size,
+  fn(np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride),
+     context_lens, num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), partition_size,
      max_partitions, part_out, part_lse, nullptr, nullptr);
   return launch_status();
 }
@@ -587,15 +695,14 @@ extern "C" int pkv_lse_combine(float* out, float* lse, const float* part_out,
                                int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
                                int32_t max_partitions, pkv_stream_t stream) {
   if (!out || !part_out || !part_lse || !context_lens) return PKV_ERR_NULL;
-  if (batch < 0 || num_q_heads <= 0 || head_dim <= 0 || head_dim > 2 * kWave ||
+  if (batch < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
       partition_size <= 0 || max_partitions <= 0)
     return PKV_ERR_SHAPE;
   if (batch == 0) return PKV_OK;
   // Lengths above max_partitions * partition_size are clamped to it.
   const int64_t cap64 = static_cast<int64_t>(max_partitions) * partition_size;
   const int cap = cap64 > (1 << 30) ? (1 << 30) : static_cast<int>(cap64);
-  hipLaunchKernelGGL(lse_combine_kernel, dim3(num_q_heads, batch), dim3(kWave), 0,
-                     static_cast<hipStream_t>(stream), out, lse, part_out, part_lse,
-                     context_lens, cap, num_q_heads, head_dim, partition_size, max_partitions, 0);
+  combine_launch(static_cast<hipStream_t>(stream), out, lse, part_out, part_lse, context_lens,
+                 batch, cap, num_q_heads, head_dim, partition_size, max_partitions, 0);
   return launch_status();
 }
