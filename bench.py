@@ -204,9 +204,12 @@ def main():
     part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
     part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
 
+    # same work order as inside the step: a plan for these lengths and this partition size
+    plan_ws = pkv.decode_plan(ctx, tables, hq, d, max_ctx, P)
+
     def pass1():
         pkv.paged_decode_partials(q, kc, vc, tables, ctx, max_ctx, P, scale=scale,
-                                  part_out=part_out, part_lse=part_lse)
+                                  part_out=part_out, part_lse=part_lse, plan_workspace=plan_ws)
 
     for _ in range(5):
         pass1()

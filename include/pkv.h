@@ -116,13 +116,29 @@ int pkv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
                   int32_t num_blocks, int32_t dtype, pkv_stream_t stream);
 
 /*
- * Bytes of device workspace pkv_paged_decode needs: the per-partition
- * partial outputs and log-sum-exps, batch * num_q_heads * P * (head_dim + 1)
- * floats (plus alignment) with P = ceil(max_context_len / partition_size).
- * 0 when partition_size is 0 or a single partition covers max_context_len.
+ * Bytes of device workspace the decode calls need (> 0 whenever batch > 0):
+ * the work plan (a count and batch * P unit entries) and, when the context is
+ * split into P = ceil(max_context_len / partition_size) > 1 partitions, the
+ * per-partition partial outputs and log-sum-exps, batch * num_q_heads * P *
+ * (head_dim + 1) floats; each part 256-byte aligned.  The workspace itself
+ * must be 256-byte aligned.
  */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Work plan of the decode's first pass, written into `workspace`: the
+ * (sequence, partition) units in longest-first order (every full partition,
+ * then each sequence's shorter last partition by decreasing length).  The
+ * order decides only which workgroup runs when; results never depend on it.
+ * Reads context_lens; lengths are clamped to bt_stride * 16.  A plan stays
+ * valid for every pkv_paged_decode_planned call with the same context_lens
+ * contents, batch, max_context_len, partition_size and workspace, e.g. all the
+ * layers of one decode step.
+ */
+int pkv_decode_plan(void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                    int64_t bt_stride, int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_context_len, int32_t partition_size, pkv_stream_t stream);
 
 /*
  * Paged decode attention (spindle: gather by block table with an explicit
@@ -146,8 +162,10 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
  * fit in one partition are written directly.  The result does not depend on
  * the batch: a sequence decoded alone or in any batch, with the same
  * partition_size, gives bit-identical out and lse.
- * lse may be NULL.  workspace may be NULL when
- * pkv_decode_workspace_bytes(...) is 0.
+ * lse may be NULL.  workspace: pkv_decode_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller; its previous contents do not matter.
+ * Launches, on `stream`: the plan kernel, the first pass, and (when split)
+ * the combine.
  */
 int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
@@ -165,7 +183,10 @@ int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
  * holds that range's normalised attention output and log-sum-exp.  For
  * n = 0, entry 0 is out = 0, lse = -inf.  Entries p >= max(1, ceil(n / P))
  * are not written (pkv_lse_combine never reads them).  Exactly one kernel
- * is launched: the first pass of pkv_paged_decode.
+ * is launched: the first pass of pkv_paged_decode.  plan_workspace: NULL, or
+ * a workspace holding a pkv_decode_plan made with the same context_lens
+ * contents, batch, max_context_len and this partition_size (> 0) — the
+ * first pass then runs in the plan's order, as inside pkv_paged_decode.
  * Requires max_partitions >= ceil(max_context_len / partition_size) >= 1
  * and partition_size > 0.
  */
@@ -175,8 +196,22 @@ int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,
                               const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, int32_t max_context_len, float scale,
-                              int32_t partition_size, int32_t max_partitions, int32_t dtype,
-                              pkv_stream_t stream);
+                              int32_t partition_size, int32_t max_partitions,
+                              const void* plan_workspace, int32_t dtype, pkv_stream_t stream);
+
+/*
+ * pkv_paged_decode without the plan kernel: the first pass takes its work
+ * order from a plan that pkv_decode_plan wrote earlier (same stream order)
+ * into the same workspace for the same context_lens contents, batch,
+ * max_context_len and partition_size.  Results are those of pkv_paged_decode.
+ */
+int pkv_paged_decode_planned(float* out, float* lse, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
+                             const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_context_len, float scale,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes,
+                             int32_t dtype, pkv_stream_t stream);
 
 /*
  * Second pass: merge partitions by log-sum-exp (flash-decoding combine).

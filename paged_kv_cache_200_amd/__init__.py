@@ -10,6 +10,7 @@ using the ops without it raises.
 from .ops import (  # noqa: F401
     BLOCK_SIZE,
     copy_blocks,
+    decode_plan,
     decode_workspace_bytes,
     describe_device_error,
     device_error,
@@ -17,6 +18,7 @@ from .ops import (  # noqa: F401
     lse_combine,
     paged_decode,
     paged_decode_partials,
+    paged_decode_planned,
 )
 from .block_manager import BlockManager, OutOfBlocks  # noqa: F401
 

@@ -47,9 +47,13 @@ SIGNATURES = {
     "pkv_paged_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                         _i32, _vp]),
+    "pkv_decode_plan": (ctypes.c_int, [_vp, _sz, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_decode_planned": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
+                                                _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                                _vp, _sz, _i32, _vp]),
     "pkv_paged_decode_partials": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                                                 _i32, _i32, _i32, _vp]),
+                                                 _i32, _i32, _vp, _i32, _vp]),
     "pkv_lse_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                        _vp]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,

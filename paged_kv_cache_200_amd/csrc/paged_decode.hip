@@ -204,8 +204,11 @@ __device__ __forceinline__ void process_block(const TokenRegs<T, D>& r,
 //   kOrderPartMajorReversed: x = KV-head group, y = sequence, z = partition counted from
 //     the last one, so the later partitions of the longest sequences are dispatched first
 //     and every sequence's first (often shortest) partition last.
+//   kOrderPlanned: x = work unit * num_kv_heads + KV head, the units taken in the order a
+//     plan kernel wrote them (longest first, see plan_kernel).
 constexpr int kOrderPartMinor = 0;
 constexpr int kOrderPartMajorReversed = 1;
+constexpr int kOrderPlanned = 2;
 
 // NW wavefronts per workgroup.  NW > 1: the waves share one (sequence, KV head,
 // partition) and take its blocks round-robin, merging through LDS at the end.  NW == 1:
@@ -218,10 +221,19 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
     const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
     int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
     int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
-    float* __restrict__ out, float* __restrict__ lse, int order) {
+    float* __restrict__ out, float* __restrict__ lse, int order,
+    const int2* __restrict__ plan, const int* __restrict__ plan_count) {
   using Gm = Geom<T, D>;
   int part, kvh, s, nx_parts;
-  if (order == kOrderPartMinor) {
+  if (order == kOrderPlanned) {
+    const int unit = blockIdx.x / num_kv_heads;
+    kvh = blockIdx.x - unit * num_kv_heads;
+    if (unit >= *plan_count) return;
+    const int2 u = plan[unit];
+    s = u.x;
+    part = u.y;
+    nx_parts = 1 << 30;  // the plan kernel reports lengths beyond max_context_len
+  } else if (order == kOrderPartMinor) {
     part = blockIdx.x; kvh = blockIdx.y; s = blockIdx.z; nx_parts = gridDim.x;
   } else {
     kvh = blockIdx.x; s = blockIdx.y; part = gridDim.z - 1 - blockIdx.z; nx_parts = gridDim.z;
@@ -526,36 +538,131 @@ void combine_launch(hipStream_t stream, float* out, float* lse, const float* par
                        skip_single);
 }
 
-using LaunchFn = void (*)(int, int, int, hipStream_t, const void*, const void*, const void*,
-                          const int32_t*, int, const int32_t*, int, int, int, float, int, int,
-                          float*, float*, float*, float*);
+// Work plan of the first pass: the (sequence, partition) units in longest-first order,
+// so the hardware dispatcher, which hands out workgroups in grid order, schedules them
+// like longest-processing-time-first list scheduling.  Every full partition (exactly
+// part_tokens tokens) comes first, in sequence order; then each sequence's last, shorter
+// partition, bucketed by its length in 16-token blocks (>> key_shift), longest bucket
+// first.  part_tokens = 0 means one unit per sequence, bucketed by its whole length.
+// The order only changes which workgroup runs when, never a unit's result.
+// One workgroup; plan holds at most batch * np entries.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = kPlanThreads;
 
-// Grid for `np` partitions: see kOrder*.
-template <int NW, int DEPTH, int kOrder, typename T, int D, int G>
-void pass1_launch(int np, int num_kv_heads, int batch, hipStream_t stream, const void* q,
-                  const void* kc, const void* vc, const int32_t* tables, int W,
+__device__ __forceinline__ int block_scan_inclusive(int* s_scan, int v) {
+  const int tid = threadIdx.x;
+  s_scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int x = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += x;
+    __syncthreads();
+  }
+  return s_scan[tid];
+}
+
+struct UnitSplit {
+  int full;     // full partitions
+  int tail;     // 1 if a shorter last unit follows them
+  int tail_len; // its length in tokens
+};
+
+__device__ __forceinline__ UnitSplit split_units(int n, int part_tokens, int np) {
+  UnitSplit u;
+  if (part_tokens > 0) {
+    u.full = min(n / part_tokens, np);
+    u.tail_len = n - u.full * part_tokens;
+    u.tail = (u.full < np) && (u.tail_len > 0 || n == 0);
+  } else {
+    u.full = 0;
+    u.tail = 1;
+    u.tail_len = n;
+  }
+  return u;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    int2* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
+    int batch, int cap, int part_tokens, int np, int key_shift) {
+  __shared__ int s_cursor[kPlanBuckets];
+  __shared__ int s_scan[kPlanThreads];
+  __shared__ int s_full_total;
+  const int tid = threadIdx.x;
+  s_cursor[tid] = 0;
+  if (tid == 0) s_full_total = 0;
+  __syncthreads();
+  auto key_of = [&](int len) {
+    return min(kPlanBuckets - 1, ((len + kBlockTokens - 1) / kBlockTokens) >> key_shift);
+  };
+  for (int base = 0; base < batch; base += kPlanThreads) {
+    const int s = base + tid;
+    UnitSplit u = {0, 0, 0};
+    if (s < batch) {
+      int n = ctx_lens[s];
+      n = n < 0 ? 0 : min(n, cap);
+      u = split_units(n, part_tokens, np);
+      if (part_tokens > 0 && n > np * part_tokens) PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
+      if (u.tail) atomicAdd(&s_cursor[key_of(u.tail_len)], 1);
+    }
+    const int incl = block_scan_inclusive(s_scan, u.full);
+    const int first = s_full_total + incl - u.full;
+    for (int p = 0; p < u.full; ++p) plan[first + p] = make_int2(s, p);
+    __syncthreads();
+    if (tid == kPlanThreads - 1) s_full_total += incl;
+    __syncthreads();
+  }
+  // Bucket start offsets, longest bucket first; thread t owns bucket kPlanBuckets-1-t.
+  const int kb = kPlanBuckets - 1 - tid;
+  const int h = s_cursor[kb];
+  const int incl = block_scan_inclusive(s_scan, h);
+  s_cursor[kb] = s_full_total + incl - h;
+  if (tid == kPlanThreads - 1) *plan_count = s_full_total + incl;
+  __syncthreads();
+  for (int s = tid; s < batch; s += kPlanThreads) {
+    int n = ctx_lens[s];
+    n = n < 0 ? 0 : min(n, cap);
+    const UnitSplit u = split_units(n, part_tokens, np);
+    if (u.tail) plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] = make_int2(s, u.full);
+  }
+}
+
+using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
+                          const int32_t*, int, const int32_t*, int, int, int, float, int, int,
+                          float*, float*, float*, float*, const int2*, const int*);
+
+// order = kOrderPlanned: plan/plan_count from plan_kernel, grid of batch * np units.
+template <int NW, int DEPTH, typename T, int D, int G>
+void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t stream,
+                  const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                   const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                   int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
-                  float* lse) {
-  const dim3 grid = kOrder == kOrderPartMinor ? dim3(np, num_kv_heads, batch)
-                                              : dim3(num_kv_heads, batch, np);
+                  float* lse, const int2* plan, const int* plan_count) {
+  dim3 grid;
+  if (order == kOrderPlanned)
+    grid = dim3(static_cast<unsigned>(num_kv_heads) * batch * np);
+  else if (order == kOrderPartMinor)
+    grid = dim3(np, num_kv_heads, batch);
+  else
+    grid = dim3(num_kv_heads, batch, np);
   hipLaunchKernelGGL((decode_pass1_kernel<T, D, G, NW, DEPTH>), grid, dim3(NW * kWave), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
-                     part_tokens, max_parts, part_out, part_lse, out, lse, kOrder);
+                     part_tokens, max_parts, part_out, part_lse, out, lse, order, plan,
+                     plan_count);
 }
 
 // The configuration the library ships: four waves share a (sequence, KV head,
-// partition), two blocks in flight per wave, later partitions dispatched first.
+// partition) unit, two blocks in flight per wave.
 template <typename T, int D, int G>
-void pass1_default(int np, int num_kv_heads, int batch, hipStream_t stream, const void* q,
-                   const void* kc, const void* vc, const int32_t* tables, int W,
+void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t stream,
+                   const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                    const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                    int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
-                   float* lse) {
-  pass1_launch<4, 2, kOrderPartMajorReversed, T, D, G>(
-      np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx, hq, hkv, nb, scale_log2,
-      part_tokens, max_parts, part_out, part_lse, out, lse);
+                   float* lse, const int2* plan, const int* plan_count) {
+  pass1_launch<4, 2, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx,
+                              hq, hkv, nb, scale_log2, part_tokens, max_parts, part_out,
+                              part_lse, out, lse, plan, plan_count);
 }
 
 template <typename T, int D>
@@ -607,6 +714,89 @@ float scale_to_log2(float scale) {
   return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
 }
 
+// Workspace: [plan count | plan entries (int2, batch * np) | partial outputs | partial lse].
+struct Workspace {
+  int* plan_count = nullptr;
+  int2* plan = nullptr;
+  float* part_out = nullptr;
+  float* part_lse = nullptr;
+  size_t bytes = 0;
+};
+
+Workspace workspace_layout(void* base, int32_t batch, int32_t hq, int32_t D, int np,
+                           bool partials) {
+  Workspace w;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  w.plan_count = reinterpret_cast<int*>(p + off);
+  off += kAlign;
+  w.plan = reinterpret_cast<int2*>(p + off);
+  off += align_up(static_cast<size_t>(batch) * np * sizeof(int2));
+  if (partials) {
+    const size_t rows = static_cast<size_t>(batch) * hq * np;
+    w.part_out = reinterpret_cast<float*>(p + off);
+    off += align_up(rows * D * sizeof(float));
+    w.part_lse = reinterpret_cast<float*>(p + off);
+    off += align_up(rows * sizeof(float));
+  }
+  w.bytes = off;
+  return w;
+}
+
+int plan_key_shift(int32_t max_context_len, int32_t part_tokens) {
+  const int longest = part_tokens > 0 ? part_tokens : max_context_len;
+  int blocks = (longest + kBlockTokens - 1) / kBlockTokens;
+  int shift = 0;
+  while ((blocks >> shift) >= kPlanBuckets) ++shift;
+  return shift;
+}
+
+int launch_plan(const Workspace& w, const int32_t* ctx, int32_t batch, int cap, int tokens,
+                int np, int32_t max_context_len, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, w.plan, w.plan_count, ctx,
+                     batch, cap, tokens, np, plan_key_shift(max_context_len, tokens));
+  return launch_status();
+}
+
+// Shared by the decode entry points: validates, then runs [plan] + pass 1 + [combine].
+int decode_impl(bool make_plan, float* out, float* lse, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
+                const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+  LaunchFn fn = nullptr;
+  int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
+                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_context_len, partition_size, dtype, &fn);
+  if (st != PKV_OK) return st;
+  if (!out) return PKV_ERR_NULL;
+  if (batch == 0) return PKV_OK;
+  const int np = num_partitions(max_context_len, partition_size);
+  const bool split = partition_size > 0 && np > 1;
+  const size_t need =
+      pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size);
+  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_ARG;
+  const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, np, split);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int tokens = split ? partition_size : 0;
+  const int cap = static_cast<int>(bt_stride) * kBlockTokens;
+  if (make_plan && (st = launch_plan(w, context_lens, batch, cap, tokens, np, max_context_len,
+                                     s)) != PKV_OK)
+    return st;
+  fn(kOrderPlanned, np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
+     static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
+     scale_to_log2(scale), tokens, np, w.part_out, w.part_lse, out, lse, w.plan, w.plan_count);
+  if ((st = launch_status()) != PKV_OK) return st;
+  if (split) {
+    combine_launch(s, out, lse, w.part_out, w.part_lse, context_lens, batch, cap, num_q_heads,
+                   head_dim, partition_size, np, 1);
+    st = launch_status();
+  }
+  return st;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -615,11 +805,32 @@ using namespace pkv;
 extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_context_len,
                                              int32_t partition_size) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   const int np = num_partitions(max_context_len, partition_size);
-  if (partition_size <= 0 || np <= 1 || batch <= 0 || num_q_heads <= 0 || head_dim <= 0)
-    return 0;
-  const size_t rows = static_cast<size_t>(batch) * num_q_heads * np;
-  return align_up(rows * head_dim * sizeof(float)) + align_up(rows * sizeof(float));
+  const bool split = partition_size > 0 && np > 1;
+  return workspace_layout(nullptr, batch, num_q_heads, head_dim, np, split).bytes;
+}
+
+extern "C" int pkv_decode_plan(void* workspace, size_t workspace_bytes,
+                               const int32_t* context_lens, int64_t bt_stride, int32_t batch,
+                               int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                               int32_t partition_size, pkv_stream_t stream) {
+  if (!workspace || !context_lens) return PKV_ERR_NULL;
+  if (batch < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
+      max_context_len < 0 || partition_size < 0 || partition_size % kBlockTokens != 0 ||
+      bt_stride <= 0 || bt_stride > (1 << 26))
+    return PKV_ERR_SHAPE;
+  if (batch == 0) return PKV_OK;
+  if (workspace_bytes <
+      pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size))
+    return PKV_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_ARG;
+  const int np = num_partitions(max_context_len, partition_size);
+  const bool split = partition_size > 0 && np > 1;
+  const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, np, split);
+  return launch_plan(w, context_lens, batch, static_cast<int>(bt_stride) * kBlockTokens,
+                     split ? partition_size : 0, np, max_context_len,
+                     static_cast<hipStream_t>(stream));
 }
 
 extern "C" int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
@@ -629,38 +840,26 @@ extern "C" int pkv_paged_decode(float* out, float* lse, const void* q, const voi
                                 int32_t block_size, int32_t num_blocks, int32_t max_context_len,
                                 float scale, int32_t partition_size, void* workspace,
                                 size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
-  LaunchFn fn = nullptr;
-  int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
-                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                             max_context_len, partition_size, dtype, &fn);
-  if (st != PKV_OK) return st;
-  if (!out) return PKV_ERR_NULL;
-  if (batch == 0) return PKV_OK;
-  const int np = num_partitions(max_context_len, partition_size);
-  const size_t need =
-      pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-  float* part_out = nullptr;
-  float* part_lse = nullptr;
-  if (need > 0) {
-    const size_t rows = static_cast<size_t>(batch) * num_q_heads * np;
-    part_out = static_cast<float*>(workspace);
-    part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align_up(rows * head_dim * sizeof(float)));
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int tokens = partition_size > 0 && np > 1 ? partition_size : 0;
-  fn(np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride),
-     context_lens, num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), tokens, np,
-     part_out, part_lse, out, lse);
-  if ((st = launch_status()) != PKV_OK) return st;
-  if (np > 1) {
-    combine_launch(s, out, lse, part_out, part_lse, context_lens, batch,
-                   static_cast<int>(bt_stride) * kBlockTokens, num_q_heads, head_dim,
-                   partition_size, np, 1);
-    st = launch_status();
-  }
-  return st;
+  return decode_impl(true, out, lse, q, k_cache, v_cache, block_tables, bt_stride, context_lens,
+                     batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                     stream);
+}
+
+extern "C" int pkv_paged_decode_planned(float* out, float* lse, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int64_t bt_stride,
+                                        const int32_t* context_lens, int32_t batch,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        int32_t max_context_len, float scale,
+                                        int32_t partition_size, void* workspace,
+                                        size_t workspace_bytes, int32_t dtype,
+                                        pkv_stream_t stream) {
+  return decode_impl(false, out, lse, q, k_cache, v_cache, block_tables, bt_stride,
+                     context_lens, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
 }
 
 extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,
@@ -671,8 +870,8 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
                                          int32_t head_dim, int32_t block_size,
                                          int32_t num_blocks, int32_t max_context_len,
                                          float scale, int32_t partition_size,
-                                         int32_t max_partitions, int32_t dtype,
-                                         pkv_stream_t stream) {
+                                         int32_t max_partitions, const void* plan_workspace,
+                                         int32_t dtype, pkv_stream_t stream) {
   LaunchFn fn = nullptr;
   int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -684,9 +883,23 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
   if (max_partitions < np) return PKV_ERR_SHAPE;
   if (batch == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  fn(np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride),
-     context_lens, num_q_heads, num_kv_heads, num_blocks, scale_to_log2(scale), partition_size,
-     max_partitions, part_out, part_lse, nullptr, nullptr);
+  const int2* plan = nullptr;
+  const int* plan_count = nullptr;
+  int order = kOrderPartMajorReversed;
+  if (plan_workspace != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(plan_workspace) & (kAlign - 1)) != 0) return PKV_ERR_ARG;
+    const Workspace w = workspace_layout(const_cast<void*>(plan_workspace), batch, num_q_heads,
+                                         head_dim, np, false);
+    plan = w.plan;
+    plan_count = w.plan_count;
+    order = kOrderPlanned;
+  }
+  // A plan made for one partition covers whole sequences; here every unit is a
+  // partition, so a single-partition plan is only valid when np == 1 as well.
+  fn(order, np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
+     static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
+     scale_to_log2(scale), partition_size, max_partitions, part_out, part_lse, nullptr, nullptr,
+     plan, plan_count);
   return launch_status();
 }
 

@@ -108,14 +108,34 @@ def _decode_checks(q, k_cache, v_cache, block_tables, context_lens):
     return B, hq, hkv, d, nb
 
 
-def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
-                 partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
-                 stream=None):
-    """Decode attention of q [B, Hq, D] over the paged caches.
+def _workspace(workspace, need, device):
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _gpu(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    if wbytes < need:
+        raise ValueError(f"workspace holds {wbytes} bytes, {need} needed")
+    if workspace.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    return workspace, wbytes
 
-    Returns (out float32 [B, Hq, D], lse float32 [B, Hq] or None).
-    max_context_len is a host-side upper bound of context_lens.
-    """
+
+def decode_plan(context_lens, block_tables, num_q_heads, head_dim, max_context_len,
+                partition_size=0, workspace=None, stream=None):
+    """Write the first pass's longest-first work plan into a (new or given) workspace."""
+    _gpu(context_lens, "context_lens", torch.int32)
+    _gpu(block_tables, "block_tables", torch.int32)
+    B = context_lens.shape[0]
+    need = decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_size)
+    workspace, wbytes = _workspace(workspace, need, context_lens.device)
+    _lib.call("pkv_decode_plan", _ptr(workspace), wbytes, _ptr(context_lens),
+              block_tables.shape[1], B, num_q_heads, head_dim, int(max_context_len),
+              int(partition_size), _stream(stream))
+    return workspace
+
+
+def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+            partition_size, out, lse, workspace, want_lse, stream):
     B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -127,20 +147,44 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
     if lse is not None:
         _gpu(lse, "lse", torch.float32)
     need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _lib.call("pkv_paged_decode", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+    workspace, wbytes = _workspace(workspace, need, q.device)
+    _lib.call(fn_name, _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
               _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d,
               BLOCK_SIZE, nb, int(max_context_len), float(scale), int(partition_size),
               _ptr(workspace), wbytes, _kv_code(k_cache), _stream(stream))
     return out, lse
 
 
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
+                 partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
+                 stream=None):
+    """Decode attention of q [B, Hq, D] over the paged caches (plan + first pass + combine).
+
+    Returns (out float32 [B, Hq, D], lse float32 [B, Hq] or None).
+    max_context_len is a host-side upper bound of context_lens.
+    """
+    return _decode("pkv_paged_decode", q, k_cache, v_cache, block_tables, context_lens,
+                   max_context_len, scale, partition_size, out, lse, workspace, want_lse, stream)
+
+
+def paged_decode_planned(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                         workspace, scale=None, partition_size=0, out=None, lse=None,
+                         want_lse=True, stream=None):
+    """paged_decode reusing a plan already written into `workspace` by decode_plan."""
+    if workspace is None:
+        raise ValueError("paged_decode_planned needs the workspace decode_plan filled")
+    return _decode("pkv_paged_decode_planned", q, k_cache, v_cache, block_tables, context_lens,
+                   max_context_len, scale, partition_size, out, lse, workspace, want_lse, stream)
+
+
 def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                           partition_size, scale=None, max_partitions=None, part_out=None,
-                          part_lse=None, stream=None):
-    """First pass only: (part_out [B, Hq, NP, D], part_lse [B, Hq, NP]) float32."""
+                          part_lse=None, plan_workspace=None, stream=None):
+    """First pass only: (part_out [B, Hq, NP, D], part_lse [B, Hq, NP]) float32.
+
+    plan_workspace: optional workspace holding a decode_plan for the same inputs and
+    partition_size; the pass then runs in the plan's order.
+    """
     B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -158,8 +202,8 @@ def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_c
     _lib.call("pkv_paged_decode_partials", _ptr(part_out), _ptr(part_lse), _ptr(q),
               _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
               _ptr(context_lens), B, hq, hkv, d, BLOCK_SIZE, nb, int(max_context_len),
-              float(scale), int(partition_size), int(max_partitions), _kv_code(k_cache),
-              _stream(stream))
+              float(scale), int(partition_size), int(max_partitions), _ptr(plan_workspace),
+              _kv_code(k_cache), _stream(stream))
     return part_out, part_lse
 
 

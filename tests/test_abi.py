@@ -46,10 +46,13 @@ def test_host_only_calls():
     assert lib.pkv_status_string(0) == b"ok"
     assert lib.pkv_status_string(-3) == b"unsupported size or shape"
     # workspace sizing is pure host arithmetic
-    assert lib.pkv_decode_workspace_bytes(4, 32, 128, 32768, 0) == 0
-    assert lib.pkv_decode_workspace_bytes(4, 32, 128, 512, 512) == 0
+    assert lib.pkv_decode_workspace_bytes(0, 32, 128, 32768, 0) == 0
+    plan_only = lib.pkv_decode_workspace_bytes(4, 32, 128, 32768, 0)
+    assert 0 < plan_only < 4096           # plan count + 4 entries, no partials
+    assert lib.pkv_decode_workspace_bytes(4, 32, 128, 512, 512) == plan_only
     ws = lib.pkv_decode_workspace_bytes(4, 32, 128, 32768, 512)
-    assert ws >= 4 * 32 * 64 * (128 + 1) * 4
+    assert ws >= 4 * 32 * 64 * (128 + 1) * 4 + 4 * 64 * 8
+    assert ws % 256 == 0
     # argument errors are reported before any launch
     st = lib.pkv_paged_decode(None, None, None, None, None, None, 1, None, 1, 8, 2, 64, 16, 4,
                               16, 1.0, 0, None, 0, 0, None)

@@ -287,3 +287,72 @@ def test_stale_slots_never_leak(fill):
     assert got[0].tobytes() == ref[0].tobytes() and got[1].tobytes() == ref[1].tobytes()
     assert_parity(got, oracle_decode(case), "f32", f"stale {fill}")
     assert_no_device_error()
+
+
+# --------------------------------------------------------------------------------------
+# Work plan: order only, never results
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_plan_reused_across_layers(P):
+    """One plan per step serves every layer: planned calls equal the all-in-one call
+    bit for bit, and the oracle within tolerance."""
+    case = config_case("qwen_gqa", 1, layers=3)
+    ops = _ops()
+    dcs = [DeviceCase(case, layer) for layer in range(3)]
+    ws = ops.decode_plan(dcs[0].ctx, dcs[0].tables, case.num_q_heads, case.head_dim,
+                         dcs[0].max_ctx, P)
+    for layer, dc in enumerate(dcs):
+        o1, l1 = ops.paged_decode_planned(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx, ws,
+                                          scale=float(case.scale), partition_size=P)
+        o2, l2 = ops.paged_decode(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                                  scale=float(case.scale), partition_size=P)
+        torch.cuda.synchronize()
+        assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes()
+        assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes()
+        assert_parity((o1.cpu().numpy(), l1.cpu().numpy()), oracle_decode(case, layer), "bf16",
+                      f"planned L{layer} P{P}")
+    assert_no_device_error()
+
+
+def test_partials_with_and_without_plan_identical():
+    case = config_case("high_concurrency", 2, max_batch=40)
+    dc = DeviceCase(case)
+    ops = _ops()
+    P = 128
+    a = ops.paged_decode_partials(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx, P,
+                                  scale=float(case.scale))
+    ws = ops.decode_plan(dc.ctx, dc.tables, case.num_q_heads, case.head_dim, dc.max_ctx, P)
+    b = ops.paged_decode_partials(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx, P,
+                                  scale=float(case.scale), plan_workspace=ws)
+    torch.cuda.synchronize()
+    live = np.zeros(a[1].shape, bool)
+    for s, n in enumerate(case.context_lens.tolist()):
+        live[s, :, :max(1, -(-n // P))] = True
+    assert a[0].cpu().numpy()[live].tobytes() == b[0].cpu().numpy()[live].tobytes()
+    assert a[1].cpu().numpy()[live].tobytes() == b[1].cpu().numpy()[live].tobytes()
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 64, 1024])
+def test_plan_lists_every_unit_once_longest_first(P):
+    """Plan layout inside the workspace: int32 count at byte 0, int2 (seq, partition)
+    entries from byte 256."""
+    lens = [0, 1, 15, 16, 17, 64, 65, 130, 1024, 1025, 3000, 5, 700, 64]
+    case = build_case("plan", lens, 8, 2, 64, "bf16", seed=3)
+    dc = DeviceCase(case)
+    ws = _ops().decode_plan(dc.ctx, dc.tables, 8, 64, dc.max_ctx, P)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    count = int(raw[:4].view(np.int32)[0])
+    ent = raw[256:256 + 8 * count].view(np.int32).reshape(-1, 2)
+    want = []
+    for s, n in enumerate(lens):
+        np_ = 1 if P == 0 else max(1, -(-n // P))
+        want += [(s, p) for p in range(np_)]
+    assert count == len(want)
+    assert sorted(map(tuple, ent.tolist())) == sorted(want)
+    size = [min(P, lens[s] - p * P) if P else lens[s] for s, p in ent.tolist()]
+    blocks = [-(-x // 16) for x in size]
+    assert blocks == sorted(blocks, reverse=True), "plan is not longest-first"
+    assert_no_device_error()
