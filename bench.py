@@ -43,12 +43,15 @@ def parse_args():
     p.add_argument("--workload", default="high_concurrency",
                    choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny"])
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--partition-size", type=int, default=1024)
+    p.add_argument("--partition-size", type=int, default=2048)
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time for the oracle baseline (repeats the whole batch)")
     p.add_argument("--no-copy-probe", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="before the timed steps, run 3 device copies of MIB MiB (a known-size "
+                        "reference for HBM traffic counters)")
     return p.parse_args()
 
 
@@ -175,6 +178,17 @@ def main():
         pkv.kv_append(kc, vc, k_new, v_new, tables, start, cu)
         pkv.paged_decode(q, kc, vc, tables, ctx, max_ctx, scale=scale, partition_size=P, out=out,
                          lse=lse, workspace=ws)
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copies: 3 x {n} bytes read + written", file=sys.stderr,
+              flush=True)
+        del src, dst
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
