@@ -182,16 +182,17 @@ def combine_partitions(part_out, part_lse):
 
 
 def kv_append(k_pool, v_pool, k_new, v_new, block_tables, start_pos, cu_new_tokens,
-              block_size: int = 16):
+              block_size: int = 16, inplace: bool = False):
     """Write new tokens' K/V into their blocks at an explicit start position.
 
     Token i of sequence s (global row cu_new_tokens[s] + i of k_new/v_new,
     [T, Hkv, D]) lands at logical position start_pos[s] + i, i.e. physical
     block block_tables[s][pos // bs], slot pos % bs, for every KV head.  A raw
-    bit copy; returns new pools and leaves the inputs untouched.
+    bit copy; returns new pools and leaves the inputs untouched, or writes into
+    the given pools when inplace=True (long replays).
     """
-    k_out = k_pool.copy()
-    v_out = v_pool.copy()
+    k_out = k_pool if inplace else k_pool.copy()
+    v_out = v_pool if inplace else v_pool.copy()
     W = block_tables.shape[1]
     NB = k_pool.shape[0]
     B = len(start_pos)
