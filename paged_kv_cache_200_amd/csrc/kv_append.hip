@@ -2,9 +2,9 @@
 // start position (spindle, "Two bugs worth recording": append takes an
 // explicit start position; the cache never infers or advances a length).
 //
-// One workgroup per new token.  The token's sequence is found by a binary
-// search over cu_new_tokens; its position gives (block, slot) through the
-// block table; then every KV head's D-element row is copied with 16-byte
+// One workgroup (one wavefront) per new token.  The token's sequence is found
+// by counting the cu_new_tokens entries at or below its index; its position
+// gives (block, slot) through the block table; then every KV head's D-element row is copied with 16-byte
 // vector moves, bit-exact.  Out-of-range positions or block ids are never
 // written: the token is skipped and an error bit is set.
 
@@ -23,13 +23,16 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
     const int32_t* __restrict__ start_pos, const int32_t* __restrict__ cu, int batch,
     int total, int num_kv_heads, int row_vecs, int num_blocks) {
   const int i = blockIdx.x;
-  // sequence s: the largest s with cu[s] <= i (empty sequences are passed over)
-  int lo = 0, hi = batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) / 2;
-    if (cu[mid] <= i) lo = mid; else hi = mid;
+  // Sequence s of token i: the largest s with cu[s] <= i, i.e. (number of entries of the
+  // non-decreasing cu[0..batch-1] that are <= i) - 1.  The lanes load the entries in
+  // parallel and count them with ballots, so the lookup costs one memory round trip.
+  int count = 0;
+  for (int j0 = 0; j0 < batch; j0 += kThreads) {
+    const int j = j0 + threadIdx.x;
+    const bool le = j < batch && cu[j] <= i;
+    count += __popcll(__ballot(le));
   }
-  const int s = lo;
+  const int s = max(count - 1, 0);
   const int c0 = cu[s], c1 = cu[s + 1];
   if (c0 > i || c1 <= i || cu[batch] != total) {
     if (threadIdx.x == 0) PKV_FLAG_ERROR(PKV_DEVERR_CU);

@@ -232,16 +232,20 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
     int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
     int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
     float* __restrict__ out, float* __restrict__ lse, int order,
-    const int2* __restrict__ plan, const int* __restrict__ plan_count) {
+    const int4* __restrict__ plan, const int* __restrict__ plan_count) {
   using Gm = Geom<T, D>;
   int part, kvh, s, nx_parts;
+  int n = 0;
   if (order == kOrderPlanned) {
+    // The plan entry carries the (already range-checked) context length: one load
+    // instead of two dependent ones before the first block-table read.
     const int unit = blockIdx.x / num_kv_heads;
     kvh = blockIdx.x - unit * num_kv_heads;
     if (unit >= *plan_count) return;
-    const int2 u = plan[unit];
+    const int4 u = plan[unit];
     s = u.x;
     part = u.y;
+    n = u.z;
     nx_parts = 1 << 30;  // the plan kernel reports lengths beyond max_context_len
   } else if (order == kOrderPartMinor) {
     part = blockIdx.x; kvh = blockIdx.y; s = blockIdx.z; nx_parts = gridDim.x;
@@ -254,11 +258,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
   const int sub = lane % kLanesPerToken;
   const bool leader = threadIdx.x == 0;
 
-  int n = ctx_lens[s];
-  const int cap = W * kBlockTokens;
-  if (n < 0 || n > cap) {
-    if (leader && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
-    n = n < 0 ? 0 : cap;
+  if (order != kOrderPlanned) {
+    n = ctx_lens[s];
+    const int cap = W * kBlockTokens;
+    if (n < 0 || n > cap) {
+      if (leader && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+      n = n < 0 ? 0 : cap;
+    }
   }
   int nparts = 1;
   int tok0 = 0, tok1 = n;
@@ -549,6 +555,7 @@ void combine_launch(hipStream_t stream, float* out, float* lse, const float* par
 }
 
 // Work plan of the first pass: the (sequence, partition) units in longest-first order,
+// each entry {sequence, partition, context length clamped to the table, 0},
 // so the hardware dispatcher, which hands out workgroups in grid order, schedules them
 // like longest-processing-time-first list scheduling.  Every full partition (exactly
 // part_tokens tokens) comes first, in sequence order; then each sequence's last, shorter
@@ -559,17 +566,22 @@ void combine_launch(hipStream_t stream, float* out, float* lse, const float* par
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = kPlanThreads;
 
-__device__ __forceinline__ int block_scan_inclusive(int* s_scan, int v) {
-  const int tid = threadIdx.x;
-  s_scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int x = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += x;
-    __syncthreads();
+// Inclusive prefix sum over the workgroup (thread order); every thread gets its own.
+// Wave-level shuffles, then one pass over the per-wave totals: two barriers.
+__device__ __forceinline__ int block_scan_inclusive(int* s_wave, int v) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int x = __shfl_up(v, off);
+    if (lane >= off) v += x;
   }
-  return s_scan[tid];
+  if (lane == kWave - 1) s_wave[wave] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  __syncthreads();
+  return v + before;
 }
 
 struct UnitSplit {
@@ -593,10 +605,10 @@ __device__ __forceinline__ UnitSplit split_units(int n, int part_tokens, int np)
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    int2* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
+    int4* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
     int batch, int cap, int part_tokens, int np, int key_shift) {
   __shared__ int s_cursor[kPlanBuckets];
-  __shared__ int s_scan[kPlanThreads];
+  __shared__ int s_scan[kPlanThreads / kWave];
   __shared__ int s_full_total;
   const int tid = threadIdx.x;
   s_cursor[tid] = 0;
@@ -605,19 +617,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   auto key_of = [&](int len) {
     return min(kPlanBuckets - 1, ((len + kBlockTokens - 1) / kBlockTokens) >> key_shift);
   };
+  auto n_clamped = [&](int seq) {
+    const int n = ctx_lens[seq];
+    return n < 0 ? 0 : min(n, cap);
+  };
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int s = base + tid;
     UnitSplit u = {0, 0, 0};
     if (s < batch) {
-      int n = ctx_lens[s];
-      n = n < 0 ? 0 : min(n, cap);
+      const int raw = ctx_lens[s];
+      if (raw < 0 || raw > cap) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+      const int n = n_clamped(s);
       u = split_units(n, part_tokens, np);
       if (part_tokens > 0 && n > np * part_tokens) PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
       if (u.tail) atomicAdd(&s_cursor[key_of(u.tail_len)], 1);
     }
     const int incl = block_scan_inclusive(s_scan, u.full);
     const int first = s_full_total + incl - u.full;
-    for (int p = 0; p < u.full; ++p) plan[first + p] = make_int2(s, p);
+    for (int p = 0; p < u.full; ++p) plan[first + p] = make_int4(s, p, n_clamped(s), 0);
     __syncthreads();
     if (tid == kPlanThreads - 1) s_full_total += incl;
     __syncthreads();
@@ -633,13 +650,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int n = ctx_lens[s];
     n = n < 0 ? 0 : min(n, cap);
     const UnitSplit u = split_units(n, part_tokens, np);
-    if (u.tail) plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] = make_int2(s, u.full);
+    if (u.tail) plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] = make_int4(s, u.full, n, 0);
   }
 }
 
 using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
                           const int32_t*, int, const int32_t*, int, int, int, float, int, int,
-                          float*, float*, float*, float*, const int2*, const int*);
+                          float*, float*, float*, float*, const int4*, const int*);
 
 // order = kOrderPlanned: plan/plan_count from plan_kernel, grid of batch * np units.
 template <int NW, int DEPTH, typename T, int D, int G>
@@ -647,7 +664,7 @@ void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t st
                   const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                   const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                   int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
-                  float* lse, const int2* plan, const int* plan_count) {
+                  float* lse, const int4* plan, const int* plan_count) {
   dim3 grid;
   if (order == kOrderPlanned)
     grid = dim3(static_cast<unsigned>(num_kv_heads) * batch * np);
@@ -669,7 +686,7 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
                    const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                    const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                    int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
-                   float* lse, const int2* plan, const int* plan_count) {
+                   float* lse, const int4* plan, const int* plan_count) {
   pass1_launch<4, 2, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx,
                               hq, hkv, nb, scale_log2, part_tokens, max_parts, part_out,
                               part_lse, out, lse, plan, plan_count);
@@ -724,10 +741,10 @@ float scale_to_log2(float scale) {
   return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
 }
 
-// Workspace: [plan count | plan entries (int2, batch * np) | partial outputs | partial lse].
+// Workspace: [plan count | plan entries (int4, batch * np) | partial outputs | partial lse].
 struct Workspace {
   int* plan_count = nullptr;
-  int2* plan = nullptr;
+  int4* plan = nullptr;
   float* part_out = nullptr;
   float* part_lse = nullptr;
   size_t bytes = 0;
@@ -740,8 +757,8 @@ Workspace workspace_layout(void* base, int32_t batch, int32_t hq, int32_t D, int
   size_t off = 0;
   w.plan_count = reinterpret_cast<int*>(p + off);
   off += kAlign;
-  w.plan = reinterpret_cast<int2*>(p + off);
-  off += align_up(static_cast<size_t>(batch) * np * sizeof(int2));
+  w.plan = reinterpret_cast<int4*>(p + off);
+  off += align_up(static_cast<size_t>(batch) * np * sizeof(int4));
   if (partials) {
     const size_t rows = static_cast<size_t>(batch) * hq * np;
     w.part_out = reinterpret_cast<float*>(p + off);
@@ -893,7 +910,7 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
   if (max_partitions < np) return PKV_ERR_SHAPE;
   if (batch == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int2* plan = nullptr;
+  const int4* plan = nullptr;
   const int* plan_count = nullptr;
   int order = kOrderPartMajorReversed;
   if (plan_workspace != nullptr) {

@@ -336,8 +336,8 @@ def test_partials_with_and_without_plan_identical():
 
 @pytest.mark.parametrize("P", [0, 64, 1024])
 def test_plan_lists_every_unit_once_longest_first(P):
-    """Plan layout inside the workspace: int32 count at byte 0, int2 (seq, partition)
-    entries from byte 256."""
+    """Plan layout inside the workspace: int32 count at byte 0, int4 (seq, partition,
+    context length, 0) entries from byte 256."""
     lens = [0, 1, 15, 16, 17, 64, 65, 130, 1024, 1025, 3000, 5, 700, 64]
     case = build_case("plan", lens, 8, 2, 64, "bf16", seed=3)
     dc = DeviceCase(case)
@@ -345,7 +345,9 @@ def test_plan_lists_every_unit_once_longest_first(P):
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     count = int(raw[:4].view(np.int32)[0])
-    ent = raw[256:256 + 8 * count].view(np.int32).reshape(-1, 2)
+    full = raw[256:256 + 16 * count].view(np.int32).reshape(-1, 4)
+    assert all(int(n) == lens[int(s_)] for s_, _, n, _ in full.tolist())
+    ent = full[:, :2]
     want = []
     for s, n in enumerate(lens):
         np_ = 1 if P == 0 else max(1, -(-n // P))
