@@ -43,7 +43,7 @@ def parse_args():
     p.add_argument("--workload", default="high_concurrency",
                    choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny"])
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--partition-size", type=int, default=2048)
+    p.add_argument("--partition-size", type=int, default=4096)
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,

@@ -209,6 +209,90 @@ __device__ __forceinline__ void process_block(const TokenRegs<T, D>& r,
   }
 }
 
+// Log-sum-exp merge of one (sequence, query head)'s partition results, by one wavefront:
+// lane p holds partition p's log-sum-exp (64 partitions per round), so the max and the
+// weight sum are wave reductions; the weighted sum of the partial outputs then streams
+// the partitions with every lane owning D/64 output dims, four partitions per step.
+// Used by the combine kernel and by the first pass's merging workgroup, so both give
+// bit-identical results.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+template <int D>
+__device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* __restrict__ lse_el,
+                                            const float* __restrict__ pl,
+                                            const float* __restrict__ po, int nparts, int lane) {
+  constexpr int kPer = D / kWave;  // output dims per lane
+  constexpr float kLog2e = 1.44269504088896340736f;
+  float M = -INFINITY;
+  for (int p0 = 0; p0 < nparts; p0 += kWave)
+    M = fmaxf(M, wave_max(p0 + lane < nparts ? pl[p0 + lane] : -INFINITY));
+  float acc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
+  float den = 0.0f;
+  for (int p0 = 0; p0 < nparts; p0 += kWave) {
+    const int cnt = min(kWave, nparts - p0);
+    const float lp = lane < cnt ? pl[p0 + lane] : -INFINITY;
+    const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
+    den += wave_sum(w);
+    int p = 0;
+    for (; p + 4 <= cnt; p += 4) {
+      float wp[4];
+      float x[4][kPer];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wp[u] = __shfl(w, p + u);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) x[u][j] = po[(p0 + p + u) * D + j * kWave + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp[u], x[u][j], acc[j]);
+    }
+    for (; p < cnt; ++p) {
+      const float wp = __shfl(w, p);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp, po[(p0 + p) * D + j * kWave + lane], acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) out_row[j * kWave + lane] = den > 0.0f ? acc[j] / den : 0.0f;
+  if (lse_el != nullptr && lane == 0) *lse_el = den > 0.0f ? M + __logf(den) : -INFINITY;
+}
+
+// Second pass as its own kernel: one wavefront per (sequence, query head), four per
+// workgroup.
+constexpr int kCombineWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
+    float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
+    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens, int batch, int cap,
+    int num_q_heads, int part_tokens, int max_parts, int skip_single) {
+  const int row = blockIdx.x * kCombineWaves + threadIdx.x / kWave;  // (s, h) flattened
+  const int lane = threadIdx.x % kWave;
+  if (row >= batch * num_q_heads) return;
+  const int s = row / num_q_heads;
+  int n = ctx_lens[s];
+  n = n < 0 ? 0 : min(n, cap);
+  int nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
+  nparts = min(nparts, max_parts);
+  if (skip_single && nparts == 1) return;
+  const size_t sh = static_cast<size_t>(row);
+  combine_row<D>(out + sh * D, lse != nullptr ? lse + sh : nullptr, part_lse + sh * max_parts,
+                 part_out + sh * max_parts * D, nparts, lane);
+}
+
 // Grid layouts of the first pass.
 //   kOrderPartMinor: x = partition, y = KV-head group, z = sequence.
 //   kOrderPartMajorReversed: x = KV-head group, y = sequence, z = partition counted from
@@ -461,82 +545,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
       }
     }
   }
-}
 
-// Second pass: merge a (sequence, query head)'s partitions by log-sum-exp.  One
-// wavefront per (sequence, query head), four per workgroup.  Lane p holds partition p's
-// log-sum-exp (64 partitions per round), so the max and the weight sum are wave
-// reductions; the weighted sum of the partial outputs then streams the partitions with
-// every lane owning D/64 output dims, four partitions per step.
-constexpr int kCombineWaves = 4;
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-template <int D>
-__global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
-    float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
-    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens, int batch, int cap,
-    int num_q_heads, int part_tokens, int max_parts, int skip_single) {
-  constexpr int kPer = D / kWave;  // output dims per lane
-  constexpr float kLog2e = 1.44269504088896340736f;
-  const int row = blockIdx.x * kCombineWaves + threadIdx.x / kWave;  // (s, h) flattened
-  const int lane = threadIdx.x % kWave;
-  if (row >= batch * num_q_heads) return;
-  const int s = row / num_q_heads;
-  int n = ctx_lens[s];
-  n = n < 0 ? 0 : min(n, cap);
-  int nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
-  nparts = min(nparts, max_parts);
-  if (skip_single && nparts == 1) return;
-  const size_t sh = static_cast<size_t>(row);
-  const float* pl = part_lse + sh * max_parts;
-  const float* po = part_out + sh * max_parts * D;
-
-  float M = -INFINITY;
-  for (int p0 = 0; p0 < nparts; p0 += kWave)
-    M = fmaxf(M, wave_max(p0 + lane < nparts ? pl[p0 + lane] : -INFINITY));
-  float acc[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
-  float den = 0.0f;
-  for (int p0 = 0; p0 < nparts; p0 += kWave) {
-    const int cnt = min(kWave, nparts - p0);
-    const float lp = lane < cnt ? pl[p0 + lane] : -INFINITY;
-    const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
-    den += wave_sum(w);
-    int p = 0;
-    for (; p + 4 <= cnt; p += 4) {
-      float wp[4];
-      float x[4][kPer];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wp[u] = __shfl(w, p + u);
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) x[u][j] = po[(p0 + p + u) * D + j * kWave + lane];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp[u], x[u][j], acc[j]);
-    }
-    for (; p < cnt; ++p) {
-      const float wp = __shfl(w, p);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp, po[(p0 + p) * D + j * kWave + lane], acc[j]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) out[sh * D + j * kWave + lane] = den > 0.0f ? acc[j] / den : 0.0f;
-  if (lse != nullptr && lane == 0) lse[sh] = den > 0.0f ? M + __logf(den) : -INFINITY;
 }
 
 void combine_launch(hipStream_t stream, float* out, float* lse, const float* part_out,
@@ -778,8 +787,9 @@ int plan_key_shift(int32_t max_context_len, int32_t part_tokens) {
   return shift;
 }
 
-int launch_plan(const Workspace& w, const int32_t* ctx, int32_t batch, int cap, int tokens,
-                int np, int32_t max_context_len, hipStream_t s) {
+int launch_plan(const Workspace& w, const int32_t* ctx, int32_t batch, int32_t hq, int cap,
+                int tokens, int np, int32_t max_context_len, hipStream_t s) {
+  (void)hq;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, w.plan, w.plan_count, ctx,
                      batch, cap, tokens, np, plan_key_shift(max_context_len, tokens));
   return launch_status();
@@ -809,13 +819,16 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int tokens = split ? partition_size : 0;
   const int cap = static_cast<int>(bt_stride) * kBlockTokens;
-  if (make_plan && (st = launch_plan(w, context_lens, batch, cap, tokens, np, max_context_len,
-                                     s)) != PKV_OK)
+  if (make_plan && (st = launch_plan(w, context_lens, batch, num_q_heads, cap, tokens, np,
+                                     max_context_len, s)) != PKV_OK)
     return st;
   fn(kOrderPlanned, np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
      static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
      scale_to_log2(scale), tokens, np, w.part_out, w.part_lse, out, lse, w.plan, w.plan_count);
   if ((st = launch_status()) != PKV_OK) return st;
+  // A separate second pass: merging inside the first pass would need device-scope
+  // fences (whole-L2 write-back and invalidate per split workgroup), measured to cost
+  // far more than this launch.
   if (split) {
     combine_launch(s, out, lse, w.part_out, w.part_lse, context_lens, batch, cap, num_q_heads,
                    head_dim, partition_size, np, 1);
@@ -855,9 +868,9 @@ extern "C" int pkv_decode_plan(void* workspace, size_t workspace_bytes,
   const int np = num_partitions(max_context_len, partition_size);
   const bool split = partition_size > 0 && np > 1;
   const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, np, split);
-  return launch_plan(w, context_lens, batch, static_cast<int>(bt_stride) * kBlockTokens,
-                     split ? partition_size : 0, np, max_context_len,
-                     static_cast<hipStream_t>(stream));
+  return launch_plan(w, context_lens, batch, num_q_heads,
+                     static_cast<int>(bt_stride) * kBlockTokens, split ? partition_size : 0, np,
+                     max_context_len, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,

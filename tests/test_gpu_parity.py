@@ -358,3 +358,49 @@ def test_plan_lists_every_unit_once_longest_first(P):
     blocks = [-(-x // 16) for x in size]
     assert blocks == sorted(blocks, reverse=True), "plan is not longest-first"
     assert_no_device_error()
+
+
+# --------------------------------------------------------------------------------------
+# The all-in-one call equals first pass + standalone combine, on every call
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [64, 512, 2048])
+def test_decode_equals_partials_plus_combine_bitwise(P):
+    case = config_case("high_concurrency", 0)
+    dc = DeviceCase(case)
+    ops = _ops()
+    fo, fl = ops.paged_decode(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                              scale=float(case.scale), partition_size=P)
+    po, pl = ops.paged_decode_partials(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx, P,
+                                       scale=float(case.scale))
+    so, sl = ops.lse_combine(po, pl, dc.ctx, P)
+    torch.cuda.synchronize()
+    # sequences that fit one partition are written straight by the first pass in both
+    assert fo.cpu().numpy().tobytes() == so.cpu().numpy().tobytes()
+    assert fl.cpu().numpy().tobytes() == sl.cpu().numpy().tobytes()
+    assert_no_device_error()
+
+
+def test_decode_repeatable_with_reused_workspace():
+    """Twenty calls on two alternating workspaces, with a plan reused in between:
+    every result bit-identical (no stale partials or plan entries leak into a call)."""
+    case = config_case("long_context", 0)
+    dc = DeviceCase(case)
+    ops = _ops()
+    P = 512
+    first = ops.paged_decode(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                             scale=float(case.scale), partition_size=P)
+    ref = (first[0].cpu().numpy().tobytes(), first[1].cpu().numpy().tobytes())
+    need = ops.decode_workspace_bytes(case.batch, case.num_q_heads, case.head_dim, dc.max_ctx, P)
+    wss = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ops.decode_plan(dc.ctx, dc.tables, case.num_q_heads, case.head_dim, dc.max_ctx, P,
+                    workspace=wss[1])
+    for i in range(20):
+        if i % 2 == 0:
+            o, l = ops.paged_decode(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                                    scale=float(case.scale), partition_size=P, workspace=wss[0])
+        else:
+            o, l = ops.paged_decode_planned(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                                            wss[1], scale=float(case.scale), partition_size=P)
+        assert (o.cpu().numpy().tobytes(), l.cpu().numpy().tobytes()) == ref, f"call {i}"
+    assert_no_device_error()
