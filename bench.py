@@ -175,9 +175,9 @@ def main():
     scale = float(case.scale)
 
     def step():
-        pkv.kv_append(kc, vc, k_new, v_new, tables, start, cu)
-        pkv.paged_decode(q, kc, vc, tables, ctx, max_ctx, scale=scale, partition_size=P, out=out,
-                         lse=lse, workspace=ws)
+        # kv_append + paged_decode in one library call (append and plan share a launch)
+        pkv.append_paged_decode(q, kc, vc, k_new, v_new, tables, start, cu, ctx, max_ctx,
+                                scale=scale, partition_size=P, out=out, lse=lse, workspace=ws)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -280,7 +280,7 @@ def main():
             "max_context_len": max_ctx,
             "num_blocks": case.num_blocks,
             "partition_size": P,
-            "step": "kv_append(1 token/seq) + paged_decode(split-KV pass 1 + LSE combine)",
+            "step": "append 1 token/seq + work plan (one launch), split-KV first pass, LSE combine",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_ctx / step_s, 1),

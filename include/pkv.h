@@ -176,6 +176,25 @@ int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
                      int32_t dtype, pkv_stream_t stream);
 
 /*
+ * One decode step in fewer launches: exactly pkv_kv_append(k_cache, v_cache,
+ * k_new, v_new, block_tables, bt_stride, start_pos, cu_new_tokens, batch,
+ * total_new, ...) followed by pkv_paged_decode(...) on the same stream, with
+ * the same arguments, results and errors.  The append and the work plan share
+ * one launch (they touch disjoint memory), then come the first pass and,
+ * when split, the combine.  context_lens must already count the appended
+ * tokens; the caller advances lengths, never the library.
+ */
+int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache, void* v_cache,
+                            const void* k_new, const void* v_new, const int32_t* block_tables,
+                            int64_t bt_stride, const int32_t* start_pos,
+                            const int32_t* cu_new_tokens, int32_t total_new,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_context_len, float scale,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            int32_t dtype, pkv_stream_t stream);
+
+/*
  * First pass only: per-partition attention, no merge.
  *   part_out : float32 [batch][num_q_heads][max_partitions][head_dim]
  *   part_lse : float32 [batch][num_q_heads][max_partitions]

@@ -9,6 +9,7 @@ using the ops without it raises.
 
 from .ops import (  # noqa: F401
     BLOCK_SIZE,
+    append_paged_decode,
     copy_blocks,
     decode_plan,
     decode_workspace_bytes,

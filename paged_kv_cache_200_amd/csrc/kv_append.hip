@@ -2,63 +2,30 @@
 // start position (spindle, "Two bugs worth recording": append takes an
 // explicit start position; the cache never infers or advances a length).
 //
-// One workgroup (one wavefront) per new token.  The token's sequence is found
-// by counting the cu_new_tokens entries at or below its index; its position
-// gives (block, slot) through the block table; then every KV head's D-element row is copied with 16-byte
-// vector moves, bit-exact.  Out-of-range positions or block ids are never
-// written: the token is skipped and an error bit is set.
+// One workgroup (one wavefront) per new token.  The token's sequence is found by
+// counting the cu_new_tokens entries at or below its index; its position gives
+// (block, slot) through the block table; then every KV head's D-element row is
+// copied with 16-byte vector moves, bit-exact.  Out-of-range positions or block ids
+// are never written: the token is skipped and an error bit is set.
 
 #include "common.h"
 
 PKV_DEFINE_ERROR_WORD(append)
 
+#include "append_row.h"
+
 namespace pkv {
 namespace {
 
-constexpr int kThreads = 64;
+constexpr int kThreads = kWave;
 
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(
     uint4* __restrict__ kc, uint4* __restrict__ vc, const uint4* __restrict__ kn,
     const uint4* __restrict__ vn, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ start_pos, const int32_t* __restrict__ cu, int batch,
     int total, int num_kv_heads, int row_vecs, int num_blocks) {
-  const int i = blockIdx.x;
-  // Sequence s of token i: the largest s with cu[s] <= i, i.e. (number of entries of the
-  // non-decreasing cu[0..batch-1] that are <= i) - 1.  The lanes load the entries in
-  // parallel and count them with ballots, so the lookup costs one memory round trip.
-  int count = 0;
-  for (int j0 = 0; j0 < batch; j0 += kThreads) {
-    const int j = j0 + threadIdx.x;
-    const bool le = j < batch && cu[j] <= i;
-    count += __popcll(__ballot(le));
-  }
-  const int s = max(count - 1, 0);
-  const int c0 = cu[s], c1 = cu[s + 1];
-  if (c0 > i || c1 <= i || cu[batch] != total) {
-    if (threadIdx.x == 0) PKV_FLAG_ERROR(PKV_DEVERR_CU);
-    return;
-  }
-  const int pos = start_pos[s] + (i - c0);
-  if (pos < 0 || pos >= W * kBlockTokens) {
-    if (threadIdx.x == 0) PKV_FLAG_ERROR(PKV_DEVERR_POSITION);
-    return;
-  }
-  const int blk = tables[static_cast<size_t>(s) * W + pos / kBlockTokens];
-  if (static_cast<unsigned>(blk) >= static_cast<unsigned>(num_blocks)) {
-    if (threadIdx.x == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-    return;
-  }
-  const int slot = pos % kBlockTokens;
-  const int n_vec = num_kv_heads * row_vecs;
-  for (int v = threadIdx.x; v < n_vec; v += kThreads) {
-    const int h = v / row_vecs;
-    const int j = v % row_vecs;
-    const size_t dst =
-        ((static_cast<size_t>(blk) * num_kv_heads + h) * kBlockTokens + slot) * row_vecs + j;
-    const size_t src = static_cast<size_t>(i) * n_vec + v;
-    kc[dst] = kn[src];
-    vc[dst] = vn[src];
-  }
+  append_token(kc, vc, kn, vn, tables, W, start_pos, cu, batch, total, num_kv_heads, row_vecs,
+               num_blocks, blockIdx.x, threadIdx.x, &g_pkv_error_word);
 }
 
 }  // namespace

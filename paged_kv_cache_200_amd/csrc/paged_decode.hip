@@ -33,6 +33,8 @@
 
 PKV_DEFINE_ERROR_WORD(decode)
 
+#include "append_row.h"
+
 namespace pkv {
 namespace {
 
@@ -613,9 +615,9 @@ __device__ __forceinline__ UnitSplit split_units(int n, int part_tokens, int np)
   return u;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    int4* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
-    int batch, int cap, int part_tokens, int np, int key_shift) {
+__device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restrict__ plan_count,
+                                           const int32_t* __restrict__ ctx_lens, int batch,
+                                           int cap, int part_tokens, int np, int key_shift) {
   __shared__ int s_cursor[kPlanBuckets];
   __shared__ int s_scan[kPlanThreads / kWave];
   __shared__ int s_full_total;
@@ -661,6 +663,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const UnitSplit u = split_units(n, part_tokens, np);
     if (u.tail) plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] = make_int4(s, u.full, n, 0);
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    int4* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
+    int batch, int cap, int part_tokens, int np, int key_shift) {
+  build_plan(plan, plan_count, ctx_lens, batch, cap, part_tokens, np, key_shift);
+}
+
+// Prologue of an append-and-decode step in one launch: workgroup 0 writes the work
+// plan (it only reads the context lengths); every other workgroup appends one new
+// token per wavefront.  The two jobs touch disjoint memory.
+constexpr int kAppendPerGroup = kPlanThreads / kWave;
+
+__global__ __launch_bounds__(kPlanThreads) void prologue_kernel(
+    int4* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
+    int batch, int cap, int part_tokens, int np, int key_shift, uint4* __restrict__ kc,
+    uint4* __restrict__ vc, const uint4* __restrict__ kn, const uint4* __restrict__ vn,
+    const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ start_pos,
+    const int32_t* __restrict__ cu, int total, int num_kv_heads, int row_vecs,
+    int num_blocks) {
+  if (blockIdx.x == 0) {
+    build_plan(plan, plan_count, ctx_lens, batch, cap, part_tokens, np, key_shift);
+    return;
+  }
+  const int i = (blockIdx.x - 1) * kAppendPerGroup + static_cast<int>(threadIdx.x) / kWave;
+  if (i >= total) return;
+  append_token(kc, vc, kn, vn, tables, W, start_pos, cu, batch, total, num_kv_heads, row_vecs,
+               num_blocks, i, static_cast<int>(threadIdx.x) % kWave, &g_pkv_error_word);
 }
 
 using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
@@ -796,12 +826,21 @@ int launch_plan(const Workspace& w, const int32_t* ctx, int32_t batch, int32_t h
 }
 
 // Shared by the decode entry points: validates, then runs [plan] + pass 1 + [combine].
+struct AppendArgs {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* start_pos = nullptr;
+  const int32_t* cu = nullptr;
+  int32_t total = 0;
+};
+
 int decode_impl(bool make_plan, float* out, float* lse, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+                size_t workspace_bytes, int32_t dtype, pkv_stream_t stream,
+                const AppendArgs* append = nullptr) {
   LaunchFn fn = nullptr;
   int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -819,9 +858,23 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int tokens = split ? partition_size : 0;
   const int cap = static_cast<int>(bt_stride) * kBlockTokens;
-  if (make_plan && (st = launch_plan(w, context_lens, batch, num_q_heads, cap, tokens, np,
-                                     max_context_len, s)) != PKV_OK)
+  if (append != nullptr && append->total > 0) {
+    const int eb = elem_bytes(dtype);
+    const int groups = 1 + (append->total + kAppendPerGroup - 1) / kAppendPerGroup;
+    hipLaunchKernelGGL(prologue_kernel, dim3(groups), dim3(kPlanThreads), 0, s, w.plan,
+                       w.plan_count, context_lens, batch, cap, tokens, np,
+                       plan_key_shift(max_context_len, tokens),
+                       static_cast<uint4*>(const_cast<void*>(k_cache)),
+                       static_cast<uint4*>(const_cast<void*>(v_cache)),
+                       static_cast<const uint4*>(append->k_new),
+                       static_cast<const uint4*>(append->v_new), block_tables,
+                       static_cast<int>(bt_stride), append->start_pos, append->cu, append->total,
+                       num_kv_heads, head_dim * eb / 16, num_blocks);
+    if ((st = launch_status()) != PKV_OK) return st;
+  } else if (make_plan && (st = launch_plan(w, context_lens, batch, num_q_heads, cap, tokens, np,
+                                            max_context_len, s)) != PKV_OK) {
     return st;
+  }
   fn(kOrderPlanned, np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
      static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
      scale_to_log2(scale), tokens, np, w.part_out, w.part_lse, out, lse, w.plan, w.plan_count);
@@ -900,6 +953,30 @@ extern "C" int pkv_paged_decode_planned(float* out, float* lse, const void* q,
                      context_lens, batch, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);
+}
+
+extern "C" int pkv_append_paged_decode(
+    float* out, float* lse, const void* q, void* k_cache, void* v_cache, const void* k_new,
+    const void* v_new, const int32_t* block_tables, int64_t bt_stride, const int32_t* start_pos,
+    const int32_t* cu_new_tokens, int32_t total_new, const int32_t* context_lens, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
+    void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+  if (total_new < 0) return PKV_ERR_SHAPE;
+  AppendArgs a;
+  if (total_new > 0) {
+    if (!k_new || !v_new || !start_pos || !cu_new_tokens) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ARG;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.start_pos = start_pos;
+    a.cu = cu_new_tokens;
+    a.total = total_new;
+  }
+  return decode_impl(true, out, lse, q, k_cache, v_cache, block_tables, bt_stride, context_lens,
+                     batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                     stream, &a);
 }
 
 extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,

@@ -177,6 +177,44 @@ def paged_decode_planned(q, k_cache, v_cache, block_tables, context_lens, max_co
                    max_context_len, scale, partition_size, out, lse, workspace, want_lse, stream)
 
 
+def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
+                        cu_new_tokens, context_lens, max_context_len, scale=None,
+                        partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
+                        stream=None):
+    """kv_append then paged_decode in one call (append and work plan share a launch).
+
+    context_lens must already count the appended tokens.
+    """
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _gpu(t, n)
+        _same_kind(k_cache, t, n)
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    _gpu(start_pos, "start_pos", torch.int32)
+    _gpu(cu_new_tokens, "cu_new_tokens", torch.int32)
+    if start_pos.shape != (B,) or cu_new_tokens.shape != (B + 1,):
+        raise ValueError("start_pos [B] and cu_new_tokens [B + 1] expected")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    _gpu(out, "out", torch.float32)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+    need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
+    workspace, wbytes = _workspace(workspace, need, q.device)
+    _lib.call("pkv_append_paged_decode", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
+              _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+              block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
+              _ptr(context_lens), B, hq, hkv, d, BLOCK_SIZE, nb, int(max_context_len),
+              float(scale), int(partition_size), _ptr(workspace), wbytes, _kv_code(k_cache),
+              _stream(stream))
+    return out, lse
+
+
 def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                           partition_size, scale=None, max_partitions=None, part_out=None,
                           part_lse=None, plan_workspace=None, stream=None):

@@ -404,3 +404,38 @@ def test_decode_repeatable_with_reused_workspace():
                                             wss[1], scale=float(case.scale), partition_size=P)
         assert (o.cpu().numpy().tobytes(), l.cpu().numpy().tobytes()) == ref, f"call {i}"
     assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 512, 4096])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_append_paged_decode_equals_separate_calls(P, kv_dtype):
+    """The one-call append + decode equals kv_append followed by paged_decode, bit for
+    bit (outputs and pools), and the oracle within tolerance."""
+    hkv, hq, d = (8, 32, 128) if kv_dtype == "bf16" else (12, 12, 64)
+    case = build_case("step", [17, 1, 700, 4097, 64, 5000], hq, hkv, d, kv_dtype, seed=P + d)
+    rng = np.random.default_rng(P)
+    B = case.batch
+    kn = rng.standard_normal((B, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((B, hkv, d)).astype(np.float32)
+    if kv_dtype == "bf16":
+        kn, vn = bf16_bits(kn), bf16_bits(vn)
+    start = (case.context_lens - 1).astype(np.int32)
+    cu = np.arange(B + 1, dtype=np.int32)
+    ops = _ops()
+    a, b = DeviceCase(case), DeviceCase(case)
+    o1, l1 = ops.append_paged_decode(a.q, a.k, a.v, dev(kn), dev(vn), a.tables, dev(start),
+                                     dev(cu), a.ctx, a.max_ctx, scale=float(case.scale),
+                                     partition_size=P)
+    ops.kv_append(b.k, b.v, dev(kn), dev(vn), b.tables, dev(start), dev(cu))
+    o2, l2 = ops.paged_decode(b.q, b.k, b.v, b.tables, b.ctx, b.max_ctx, scale=float(case.scale),
+                              partition_size=P)
+    torch.cuda.synchronize()
+    assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes()
+    assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes()
+    assert a.k.cpu().numpy().tobytes() == b.k.cpu().numpy().tobytes()
+    assert a.v.cpu().numpy().tobytes() == b.v.cpu().numpy().tobytes()
+    kp, vp = pa.kv_append(case.k_pool[0], case.v_pool[0], kn, vn, case.block_tables, start, cu)
+    want = pa.paged_decode(case.q[0], kp, vp, case.block_tables, case.context_lens, case.scale,
+                           kv_dtype)
+    assert_parity((o1.cpu().numpy(), l1.cpu().numpy()), want, kv_dtype, f"append+decode P{P}")
+    assert_no_device_error()
