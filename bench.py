@@ -41,9 +41,11 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="high_concurrency",
-                   choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny"])
+                   choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny",
+                            "gpt2_replay"])
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--partition-size", type=int, default=4096)
+    p.add_argument("--partition-size", type=int, default=4096,
+                   help="KV partition size (the long-context workload fixes 512, tiny uses 0)")
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -119,10 +121,119 @@ def cpu_baseline(case, decode_bytes, target_s):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"whole {case.name} batch ({case.batch} sequences, sum ctx "
+        "sample": (f"whole {case.name} batch, layer 0 ({case.batch} sequences, sum ctx "
                    f"{int(case.context_lens.sum())}), decode only, float64 numpy, {reps} rep(s), "
                    f"{sec:.2f} s each; host affinity {len(os.sched_getaffinity(0))} cpus"),
         "seq_tokens_per_s": round(float(case.context_lens.sum()) / sec, 1),
+    }
+
+
+def unique_kv_tokens(case):
+    """Tokens whose K/V must come from HBM at least once: each physical block counted
+    once, with the largest number of valid slots any sequence uses in it."""
+    valid = {}
+    for s, n in enumerate(case.context_lens.tolist()):
+        for j in range(-(-n // 16)):
+            b = int(case.block_tables[s, j])
+            valid[b] = max(valid.get(b, 0), min(16, n - 16 * j))
+    return sum(valid.values())
+
+
+def run_replay(args, np, torch, pkv):
+    """The GPT-2-shaped continuous-batching replay, end to end (host block manager,
+    table uploads and every layer's append + decode), timed on the wall clock."""
+    from workloads import replay_schedule, replay_step_values
+    sched = replay_schedule(args.seed)
+    L, hq, hkv, d, nb, bs = (sched.layers, sched.num_q_heads, sched.num_kv_heads, sched.head_dim,
+                             sched.num_blocks, sched.block_size)
+    W = -(-(128 + 192) // bs)
+    kc = torch.zeros((L, nb, hkv, bs, d), dtype=torch.float32, device="cuda")
+    vc = torch.zeros_like(kc)
+    B = sched.batch
+    steps = sched.steps
+    # every step's inputs are drawn and uploaded before the timed region
+    q_all, kv_all, plan = [], [], []
+    for t in range(steps):
+        active = [s for s in range(B) if t < int(sched.gen_lens[s])]
+        plan.append(active)
+        q_all.append([torch.from_numpy(replay_step_values(sched, t, l, active, "q")).cuda()
+                      for l in range(L)])
+        kv_all.append([tuple(torch.from_numpy(x).cuda()
+                             for x in replay_step_values(sched, t, l, active, "kv"))
+                       for l in range(L)])
+    bm = pkv.BlockManager(nb, bs, free_order=sched.free_order)
+    ids = [bm.add_sequence() for _ in range(B)]
+    for s in range(B):
+        bm.prepare_write(ids[s], 0, int(sched.prompt_lens[s]))
+    tables = torch.from_numpy(bm.tables(ids, W)).cuda()
+    cu = torch.from_numpy(
+        np.concatenate([[0], np.cumsum(sched.prompt_lens)]).astype(np.int32)).cuda()
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for l in range(L):
+        k, v = replay_step_values(sched, -1, l, list(range(B)), "kv")
+        pkv.kv_append(kc[l], vc[l], torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                      tables, zero, cu)
+    torch.cuda.synchronize()
+    total_bytes, total_tokens, calls = 0, 0, 0
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pkv.decode_workspace_bytes(B, hq, d, 320, 0), dtype=torch.uint8,
+                     device="cuda")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for t in range(steps):
+        active = plan[t]
+        pos = np.array([int(sched.prompt_lens[s]) + t for s in active], np.int32)
+        for s, p_ in zip(active, pos):
+            bm.prepare_write(ids[s], int(p_), 1)
+        n = len(active)
+        host = np.concatenate([bm.tables([ids[s] for s in active], W).reshape(-1), pos, pos + 1,
+                               np.arange(n + 1, dtype=np.int32)])
+        dev_all = torch.from_numpy(host).cuda()
+        d_tables = dev_all[:n * W].view(n, W)
+        d_start = dev_all[n * W:n * W + n]
+        d_ctx = dev_all[n * W + n:n * W + 2 * n]
+        d_cu = dev_all[n * W + 2 * n:]
+        max_ctx = int(pos.max()) + 1
+        for l in range(L):
+            k, v = kv_all[t][l]
+            pkv.append_paged_decode(q_all[t][l], kc[l], vc[l], k, v, d_tables, d_start, d_cu,
+                                    d_ctx, max_ctx, partition_size=0, out=out[:n],
+                                    want_lse=False, workspace=ws)
+            calls += 1
+        ctxs = (pos + 1).astype(np.int64)
+        total_tokens += L * int(ctxs.sum())
+        total_bytes += L * (int(ctxs.sum()) * 2 * hkv * d * 4 + n * (hq * d * 4 * 2 + 4) +
+                            int(((ctxs + 15) // 16).sum()) * 4 + n * (2 * 2 * hkv * d * 4 + 12))
+        for s in active:
+            if t == int(sched.gen_lens[s]) - 1:
+                bm.free_sequence(ids[s])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
+    return {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) + seq-tokens/s at 1 GPU",
+        "value": round(total_bytes / wall / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": 0,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "gpt2_replay", "seed": args.seed, "batch": B, "layers": L,
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
+                   "num_blocks": nb, "steps": steps,
+                   "step": "host block manager + table upload + per layer append+decode"},
+        "pct_of_hbm_peak": round(100 * total_bytes / wall / 1e9 / HBM_PEAK_GBPS, 3),
+        "seq_tokens_per_s": round(total_tokens / wall, 1),
+        "gpu_event_seconds": round(gpu_s, 5),
+        "wall_seconds": round(wall, 5),
+        "decode_calls": calls,
+        "algorithmic_bytes": total_bytes,
+        "note": "launch- and host-bound: each layer call moves about 6 MB",
     }
 
 
@@ -143,19 +254,27 @@ def main():
     import paged_kv_cache_200_amd as pkv
     from workloads import bf16_bits, config_case, parallel_normal
 
+    if args.workload == "gpt2_replay":
+        print(json.dumps(run_replay(args, np, torch, pkv)), flush=True)
+        return
+
     print(f"[bench] building inputs: {args.workload} seed {args.seed}", file=sys.stderr, flush=True)
     case = config_case(args.workload, args.seed)
     P = case.extra.get("partition_size", args.partition_size)
+    if args.workload == "tiny":
+        P = 0
     B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    layers = case.layers
 
     def to_dev(x):
         if x.dtype == np.uint16:
             x = x.view(np.int16)
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
-    q = to_dev(case.q[0])
-    kc = to_dev(case.k_pool[0])
-    vc = to_dev(case.v_pool[0])
+    qs = [to_dev(case.q[l]) for l in range(layers)]
+    kcs = [to_dev(case.k_pool[l]) for l in range(layers)]
+    vcs = [to_dev(case.v_pool[l]) for l in range(layers)]
+    q, kc, vc = qs[0], kcs[0], vcs[0]
     tables = to_dev(case.block_tables)
     ctx = to_dev(case.context_lens)
     max_ctx = int(case.context_lens.max())
@@ -175,9 +294,12 @@ def main():
     scale = float(case.scale)
 
     def step():
-        # kv_append + paged_decode in one library call (append and plan share a launch)
-        pkv.append_paged_decode(q, kc, vc, k_new, v_new, tables, start, cu, ctx, max_ctx,
-                                scale=scale, partition_size=P, out=out, lse=lse, workspace=ws)
+        # per layer: kv_append + paged_decode in one library call (append and work plan
+        # share a launch)
+        for l in range(layers):
+            pkv.append_paged_decode(qs[l], kcs[l], vcs[l], k_new, v_new, tables, start, cu, ctx,
+                                    max_ctx, scale=scale, partition_size=P, out=out, lse=lse,
+                                    workspace=ws)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -213,17 +335,22 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
 
-    # the first pass alone: same kernel and partitioning, partial outputs only
+    # the first pass alone, in the step's work order: partial outputs when the context is
+    # split, else the planned decode, which is then that single launch
     np_max = max(1, -(-max_ctx // P)) if P > 0 else 1
-    part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
-    part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
-
-    # same work order as inside the step: a plan for these lengths and this partition size
     plan_ws = pkv.decode_plan(ctx, tables, hq, d, max_ctx, P)
+    if np_max > 1:
+        part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
+        part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
 
-    def pass1():
-        pkv.paged_decode_partials(q, kc, vc, tables, ctx, max_ctx, P, scale=scale,
-                                  part_out=part_out, part_lse=part_lse, plan_workspace=plan_ws)
+        def pass1():
+            pkv.paged_decode_partials(q, kc, vc, tables, ctx, max_ctx, P, scale=scale,
+                                      part_out=part_out, part_lse=part_lse,
+                                      plan_workspace=plan_ws)
+    else:
+        def pass1():
+            pkv.paged_decode_planned(q, kc, vc, tables, ctx, max_ctx, plan_ws, scale=scale,
+                                     partition_size=P, out=out, lse=lse)
 
     for _ in range(5):
         pass1()
@@ -240,21 +367,25 @@ def main():
         raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
 
     decode_bytes, append_bytes = algorithmic_bytes(case, B)
+    # shared (copy-on-write) blocks need to come from HBM once per call
+    logical_tokens = int(case.context_lens.sum())
+    unique_tokens = unique_kv_tokens(case) if case.shared_blocks else logical_tokens
+    kv_tok = 2 * hkv * d * case.elem_bytes
+    p1_bytes = decode_bytes - (logical_tokens - unique_tokens) * kv_tok
     step_s = ms_per_step / 1e3
-    value = (decode_bytes + append_bytes) / step_s / 1e9
-    # pass 1 moves the decode bytes except the final out/lse, plus its partial results
-    p1_bytes = decode_bytes
+    step_bytes = layers * (p1_bytes + append_bytes)
+    value = step_bytes / step_s / 1e9
     achieved = p1_bytes / pass1_s / 1e9
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile() if args.workload == "high_concurrency" and P == 4096 else None
 
     probe = None if args.no_copy_probe else copy_probe(torch)
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(case, decode_bytes, args.cpu_seconds)
+        cpu = cpu_baseline(case, p1_bytes, args.cpu_seconds)
 
-    sum_ctx = int(case.context_lens.sum())
+    sum_ctx = layers * logical_tokens
     line = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + seq-tokens/s at 1 GPU",
         "value": round(value, 2),
@@ -279,13 +410,16 @@ def main():
             "sum_context_tokens": sum_ctx,
             "max_context_len": max_ctx,
             "num_blocks": case.num_blocks,
+            "layers": layers,
             "partition_size": P,
             "step": "append 1 token/seq + work plan (one launch), split-KV first pass, LSE combine",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_ctx / step_s, 1),
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, p)), 5) for p in (10, 50, 90)],
-        "algorithmic_bytes_per_step": decode_bytes + append_bytes,
+        "algorithmic_bytes_per_step": step_bytes,
+        "logical_kv_bytes_per_layer": logical_tokens * kv_tok,
+        "unique_kv_bytes_per_layer": unique_tokens * kv_tok,
         "roofline": {
             "kernel": "decode_pass1_kernel",
             "bound": "hbm",
