@@ -81,7 +81,8 @@ enum pkv_device_error_bits {
   PKV_DEVERR_POSITION = 2,      /* an append position outside the table row      */
   PKV_DEVERR_CONTEXT = 4,       /* context_lens[s] < 0 or > bt_stride*block_size */
   PKV_DEVERR_MAX_CONTEXT = 8,   /* context_lens[s] > the max_context_len given   */
-  PKV_DEVERR_CU = 16            /* cu_new_tokens not non-decreasing / bad total  */
+  PKV_DEVERR_CU = 16,           /* cu_new_tokens not non-decreasing / bad total  */
+  PKV_DEVERR_GROUPS = 32        /* fork groups do not tile the batch in order    */
 };
 
 /* Library version, e.g. 100 for 1.0.0. */
@@ -193,6 +194,45 @@ int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache
                             int32_t num_blocks, int32_t max_context_len, float scale,
                             int32_t partition_size, void* workspace, size_t workspace_bytes,
                             int32_t dtype, pkv_stream_t stream);
+
+/*
+ * Decode for a batch holding copy-on-write fork groups (spindle, "Paging":
+ * forked sequences share blocks through reference counts).  Computes the
+ * same out and lse as pkv_paged_decode (equal within rounding; the shared
+ * prefix adds a partition boundary, so not bit for bit), but each group's
+ * shared leading blocks are streamed by one workgroup for all its members.
+ *
+ *   group_starts        : int32 [num_groups + 1]: group g is sequences
+ *                         [group_starts[g], group_starts[g + 1]); the groups
+ *                         tile 0..batch-1 in order (group_starts[0] = 0,
+ *                         group_starts[num_groups] = batch).  A sequence that
+ *                         shares nothing is a group of one.
+ *   group_shared_blocks : int32 [num_groups]: leading logical blocks that
+ *                         every member of g holds in common (same block ids).
+ *                         A hint for efficiency only: every member is read
+ *                         through its own table, so results never depend on
+ *                         it.  Values above max_shared_blocks (host) are
+ *                         clamped; the rest is attended as private context.
+ * Each member's tokens [shared, context_lens[s]) are split into partitions
+ * of partition_size (0: one) after the shared prefix's own partitions.
+ * workspace: pkv_shared_prefix_workspace_bytes(...) bytes, 256-byte aligned.
+ * Malformed groups set PKV_DEVERR_GROUPS (results then unspecified).
+ * Launches: plan, shared-prefix pass, first pass, combine.
+ */
+size_t pkv_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size);
+
+int pkv_paged_decode_shared_prefix(float* out, float* lse, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   int64_t bt_stride, const int32_t* context_lens,
+                                   const int32_t* group_starts,
+                                   const int32_t* group_shared_blocks, int32_t num_groups,
+                                   int32_t max_shared_blocks, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks,
+                                   int32_t max_context_len, float scale, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes, int32_t dtype,
+                                   pkv_stream_t stream);
 
 /*
  * First pass only: per-partition attention, no merge.

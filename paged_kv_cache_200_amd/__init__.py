@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     paged_decode,
     paged_decode_partials,
     paged_decode_planned,
+    paged_decode_shared_prefix,
 )
 from .block_manager import BlockManager, OutOfBlocks  # noqa: F401
 

@@ -28,6 +28,7 @@ DEVICE_ERROR_BITS = {
     4: "context length < 0 or beyond the block table",
     8: "context length above max_context_len",
     16: "cu_new_tokens malformed",
+    32: "fork groups do not tile the batch",
 }
 
 _i32 = ctypes.c_int32
@@ -54,6 +55,11 @@ SIGNATURES = {
     "pkv_append_paged_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                                                _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                                                      _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                      _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                                      _i32, _vp]),
     "pkv_paged_decode_partials": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                                  _i32, _i32, _vp, _i32, _vp]),

@@ -107,14 +107,19 @@ struct GroupState {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// K/V are read exactly once per call: non-temporal 16-byte loads keep the stream from
-// displacing other data in the caches (measured ~10% more HBM throughput on gfx950 for
-// random 4 KiB tiles than plain loads).
-__device__ __forceinline__ u32x4_t stream_load16(const void* p) {
-  return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+// K/V that are read exactly once per call go through non-temporal 16-byte loads, which
+// keep the stream from displacing other data in the caches (measured ~10% more HBM
+// throughput on gfx950 for random 4 KiB tiles than plain loads).  Blocks shared by
+// several sequences are read with plain loads so sibling waves find them cached.
+template <bool kStreaming>
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  if constexpr (kStreaming)
+    return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  else
+    return *static_cast<const u32x4_t*>(p);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kStreaming>
 __device__ __forceinline__ void load_block(TokenRegs<T, D>& r, const T* __restrict__ kt,
                                            const T* __restrict__ vt, int lane_off) {
   using Gm = Geom<T, D>;
@@ -123,8 +128,8 @@ __device__ __forceinline__ void load_block(TokenRegs<T, D>& r, const T* __restri
 #pragma unroll
     for (int c = 0; c < Gm::kChunks; ++c) {
       const int off = lane_off + i * kGroups * D + c * Gm::kChunkStride;
-      const u32x4_t kk = stream_load16(kt + off);
-      const u32x4_t vv = stream_load16(vt + off);
+      const u32x4_t kk = load16<kStreaming>(kt + off);
+      const u32x4_t vv = load16<kStreaming>(vt + off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         r.k[i][4 * c + j] = kk[j];
@@ -276,93 +281,48 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
 // workgroup.
 constexpr int kCombineWaves = 4;
 
+// nslots (nullable): per sequence, the number of slots to merge, 0 when the first pass
+// wrote the sequence's result itself; without it the count follows from the length.
 template <int D>
 __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
     float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
-    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens, int batch, int cap,
-    int num_q_heads, int part_tokens, int max_parts, int skip_single) {
+    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ nslots, int batch, int cap, int num_q_heads, int part_tokens,
+    int max_parts, int skip_single) {
   const int row = blockIdx.x * kCombineWaves + threadIdx.x / kWave;  // (s, h) flattened
   const int lane = threadIdx.x % kWave;
   if (row >= batch * num_q_heads) return;
   const int s = row / num_q_heads;
-  int n = ctx_lens[s];
-  n = n < 0 ? 0 : min(n, cap);
-  int nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
-  nparts = min(nparts, max_parts);
-  if (skip_single && nparts == 1) return;
+  int nparts;
+  if (nslots != nullptr) {
+    nparts = min(nslots[s], max_parts);
+    if (nparts <= 0) return;
+  } else {
+    int n = ctx_lens[s];
+    n = n < 0 ? 0 : min(n, cap);
+    nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
+    nparts = min(nparts, max_parts);
+    if (skip_single && nparts == 1) return;
+  }
   const size_t sh = static_cast<size_t>(row);
   combine_row<D>(out + sh * D, lse != nullptr ? lse + sh : nullptr, part_lse + sh * max_parts,
                  part_out + sh * max_parts * D, nparts, lane);
 }
 
-// Grid layouts of the first pass.
-//   kOrderPartMinor: x = partition, y = KV-head group, z = sequence.
-//   kOrderPartMajorReversed: x = KV-head group, y = sequence, z = partition counted from
-//     the last one, so the later partitions of the longest sequences are dispatched first
-//     and every sequence's first (often shortest) partition last.
-//   kOrderPlanned: x = work unit * num_kv_heads + KV head, the units taken in the order a
-//     plan kernel wrote them (longest first, see plan_kernel).
-constexpr int kOrderPartMinor = 0;
-constexpr int kOrderPartMajorReversed = 1;
-constexpr int kOrderPlanned = 2;
-
-// NW wavefronts per workgroup.  NW > 1: the waves share one (sequence, KV head,
-// partition) and take its blocks round-robin, merging through LDS at the end.  NW == 1:
-// one wave owns the unit and writes its result straight from registers.
-// DEPTH: 16-token blocks whose loads are in flight per wave (1 being processed,
-// DEPTH - 1 prefetched).
-template <typename T, int D, int G, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-    const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
-    int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
-    int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
-    float* __restrict__ out, float* __restrict__ lse, int order,
-    const int4* __restrict__ plan, const int* __restrict__ plan_count) {
+// One wave's share of a unit: attend this KV head's G query rows of sequence s over the
+// tokens [tok0, tok1) (tok0 a multiple of the block size, tok0 <= tok1), taking the range's full blocks wave, wave + NW, ... (and the trailing
+// partial block if it falls to this wave), then merge the wave's 8 token groups so that
+// every lane holds the wave's totals (m, l, acc) for its dims.
+template <typename T, int D, int G, int NW, int DEPTH, bool kStreaming>
+__device__ __forceinline__ void attend_range(GroupState<T, D, G>& st, const T* __restrict__ q,
+                                             const T* __restrict__ kc, const T* __restrict__ vc,
+                                             const int32_t* __restrict__ tables, int W, int s,
+                                             int kvh, int num_q_heads, int num_kv_heads,
+                                             int num_blocks, float scale_log2, int tok0,
+                                             int tok1, int wave, int lane) {
   using Gm = Geom<T, D>;
-  int part, kvh, s, nx_parts;
-  int n = 0;
-  if (order == kOrderPlanned) {
-    // The plan entry carries the (already range-checked) context length: one load
-    // instead of two dependent ones before the first block-table read.
-    const int unit = blockIdx.x / num_kv_heads;
-    kvh = blockIdx.x - unit * num_kv_heads;
-    if (unit >= *plan_count) return;
-    const int4 u = plan[unit];
-    s = u.x;
-    part = u.y;
-    n = u.z;
-    nx_parts = 1 << 30;  // the plan kernel reports lengths beyond max_context_len
-  } else if (order == kOrderPartMinor) {
-    part = blockIdx.x; kvh = blockIdx.y; s = blockIdx.z; nx_parts = gridDim.x;
-  } else {
-    kvh = blockIdx.x; s = blockIdx.y; part = gridDim.z - 1 - blockIdx.z; nx_parts = gridDim.z;
-  }
-  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
   const int grp = lane / kLanesPerToken;
   const int sub = lane % kLanesPerToken;
-  const bool leader = threadIdx.x == 0;
-
-  if (order != kOrderPlanned) {
-    n = ctx_lens[s];
-    const int cap = W * kBlockTokens;
-    if (n < 0 || n > cap) {
-      if (leader && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
-      n = n < 0 ? 0 : cap;
-    }
-  }
-  int nparts = 1;
-  int tok0 = 0, tok1 = n;
-  if (part_tokens > 0) {
-    nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
-    tok0 = part * part_tokens;
-    tok1 = min(n, tok0 + part_tokens);
-  }
-  if (part == nx_parts - 1 && nparts > nx_parts && leader && kvh == 0)
-    PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
-  if (part >= nparts) return;
-
   // Query rows of this KV head's group, this lane's dims, raw bits.
   uint32_t qr[G][Gm::kWords];
 #pragma unroll
@@ -377,7 +337,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
     }
   }
 
-  GroupState<T, D, G> st;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     st.m[g] = -INFINITY;
@@ -421,7 +380,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
     return __builtin_amdgcn_readlane(ids, k - id_base);
   };
   auto load = [&](TokenRegs<T, D>& r, int blk) {
-    load_block<T, D>(r, kbase + static_cast<size_t>(blk) * block_elems,
+    load_block<T, D, kStreaming>(r, kbase + static_cast<size_t>(blk) * block_elems,
                      vbase + static_cast<size_t>(blk) * block_elems, lane_off);
   };
 
@@ -476,7 +435,90 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
     st.m[g] = mx;
   }
 
-  const bool direct = (nparts == 1) && (out != nullptr);
+}
+
+// Grid layouts of the first pass.
+//   kOrderPartMinor: x = partition, y = KV-head group, z = sequence.
+//   kOrderPartMajorReversed: x = KV-head group, y = sequence, z = partition counted from
+//     the last one, so the later partitions of the longest sequences are dispatched first
+//     and every sequence's first (often shortest) partition last.
+//   kOrderPlanned: x = work unit * num_kv_heads + KV head, the units taken in the order a
+//     plan kernel wrote them (longest first, see plan_kernel).
+constexpr int kOrderPartMinor = 0;
+constexpr int kOrderPartMajorReversed = 1;
+constexpr int kOrderPlanned = 2;
+// Plan entry {sequence, first token, end token, slot | kDirectFlag}: the unit's token range,
+// the partial-result slot it fills, and whether it is its sequence's only unit (then it
+// writes out / lse itself).
+constexpr int kDirectFlag = 1 << 30;
+constexpr int kSlotMask = kDirectFlag - 1;
+
+// NW wavefronts per workgroup.  NW > 1: the waves share one (sequence, KV head,
+// partition) and take its blocks round-robin, merging through LDS at the end.  NW == 1:
+// one wave owns the unit and writes its result straight from registers.
+// DEPTH: 16-token blocks whose loads are in flight per wave (1 being processed,
+// DEPTH - 1 prefetched).
+template <typename T, int D, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
+    int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
+    int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
+    float* __restrict__ out, float* __restrict__ lse, int order,
+    const int4* __restrict__ plan, const int* __restrict__ plan_count) {
+  using Gm = Geom<T, D>;
+  int part, kvh, s;  // part: the partial-result slot written unless `direct`
+  int tok0, tok1;    // the unit's token range
+  bool direct;       // the unit is its sequence's only one: write out / lse
+  const bool leader = threadIdx.x == 0;
+  if (order == kOrderPlanned) {
+    // The plan entry carries the unit's (range-checked) token range and slot: one load
+    // instead of dependent ones before the first block-table read.
+    const int unit = blockIdx.x / num_kv_heads;
+    kvh = blockIdx.x - unit * num_kv_heads;
+    if (unit >= *plan_count) return;
+    const int4 u = plan[unit];
+    s = u.x;
+    tok0 = u.y;
+    tok1 = u.z;
+    part = u.w & kSlotMask;
+    direct = (u.w & kDirectFlag) != 0 && out != nullptr;
+  } else {
+    int nx_parts;
+    if (order == kOrderPartMinor) {
+      part = blockIdx.x; kvh = blockIdx.y; s = blockIdx.z; nx_parts = gridDim.x;
+    } else {
+      kvh = blockIdx.x; s = blockIdx.y; part = gridDim.z - 1 - blockIdx.z; nx_parts = gridDim.z;
+    }
+    int n = ctx_lens[s];
+    const int cap = W * kBlockTokens;
+    if (n < 0 || n > cap) {
+      if (leader && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+      n = n < 0 ? 0 : cap;
+    }
+    int nparts = 1;
+    tok0 = 0;
+    tok1 = n;
+    if (part_tokens > 0) {
+      nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
+      tok0 = part * part_tokens;
+      tok1 = min(n, tok0 + part_tokens);
+    }
+    if (part == nx_parts - 1 && nparts > nx_parts && leader && kvh == 0)
+      PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
+    if (part >= nparts) return;
+    direct = nparts == 1 && out != nullptr;
+  }
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+
+  GroupState<T, D, G> st;
+  attend_range<T, D, G, NW, DEPTH, true>(st, q, kc, vc, tables, W, s, kvh, num_q_heads,
+                                         num_kv_heads, num_blocks, scale_log2, tok0, tok1, wave,
+                                         lane);
+  const int grp = lane / kLanesPerToken;
+  const int sub = lane % kLanesPerToken;
+
   if constexpr (NW == 1) {
     // Lanes of token group 0 hold the totals for their dims: write them.
     if (grp == 0) {
@@ -551,18 +593,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
 }
 
 void combine_launch(hipStream_t stream, float* out, float* lse, const float* part_out,
-                    const float* part_lse, const int32_t* ctx, int batch, int cap, int hq, int D,
-                    int part_tokens, int max_parts, int skip_single) {
+                    const float* part_lse, const int32_t* ctx, const int32_t* nslots, int batch,
+                    int cap, int hq, int D, int part_tokens, int max_parts, int skip_single) {
   const int rows = batch * hq;
   const dim3 grid((rows + kCombineWaves - 1) / kCombineWaves);
   if (D == 64)
     hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineWaves * kWave), 0, stream, out,
-                       lse, part_out, part_lse, ctx, batch, cap, hq, part_tokens, max_parts,
-                       skip_single);
+                       lse, part_out, part_lse, ctx, nslots, batch, cap, hq, part_tokens,
+                       max_parts, skip_single);
   else
     hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineWaves * kWave), 0, stream,
-                       out, lse, part_out, part_lse, ctx, batch, cap, hq, part_tokens, max_parts,
-                       skip_single);
+                       out, lse, part_out, part_lse, ctx, nslots, batch, cap, hq, part_tokens,
+                       max_parts, skip_single);
 }
 
 // Work plan of the first pass: the (sequence, partition) units in longest-first order,
@@ -595,29 +637,85 @@ __device__ __forceinline__ int block_scan_inclusive(int* s_wave, int v) {
   return v + before;
 }
 
-struct UnitSplit {
-  int full;     // full partitions
-  int tail;     // 1 if a shorter last unit follows them
-  int tail_len; // its length in tokens
+// What the plan needs to know about one call.  With fork groups (shared-prefix decode),
+// every sequence's leading group_shared_blocks[g] blocks are attended by the shared
+// kernel into slots [0, nsp), and only the rest of its context becomes plan units.
+struct PlanInput {
+  const int32_t* ctx;
+  int batch;
+  int cap;          // table capacity in tokens: lengths are clamped to it
+  int part_tokens;  // 0: one unit per sequence (or per private range)
+  int max_slots;    // partial-result slots per (sequence, head)
+  int key_shift;    // length bucket = blocks >> key_shift
+  const int32_t* group_starts;         // nullable: no fork groups
+  const int32_t* group_shared_blocks;
+  int num_groups;
+  int max_shared_blocks;  // shared lengths are clamped to this and to the table width
 };
 
-__device__ __forceinline__ UnitSplit split_units(int n, int part_tokens, int np) {
-  UnitSplit u;
-  if (part_tokens > 0) {
-    u.full = min(n / part_tokens, np);
-    u.tail_len = n - u.full * part_tokens;
-    u.tail = (u.full < np) && (u.tail_len > 0 || n == 0);
+// Tokens of group g's shared prefix that the shared pass attends, clamped exactly as the
+// shared pass clamps them (blocks past the bound stay private: still correct, less shared).
+__device__ __forceinline__ int shared_prefix_tokens(int blocks, int max_blocks, int W) {
+  return max(0, min(blocks, min(max_blocks, W))) * kBlockTokens;
+}
+
+// A sequence's units: `full` partitions of part_tokens tokens starting at `base`, then
+// (tail == 1) one shorter unit of tail_len tokens (an empty one when the sequence has no
+// tokens and nothing shared).  Slots: nsp shared ones first, then one per unit.
+struct SeqUnits {
+  int n, base, nsp, full, tail, tail_len;
+};
+
+__device__ __forceinline__ int group_of(const PlanInput& in, int s) {
+  int lo = 0, hi = in.num_groups;  // largest g with group_starts[g] <= s
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (in.group_starts[mid] <= s) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int shared_slots(int shared_tokens, int part_tokens) {
+  if (shared_tokens <= 0) return 0;
+  return part_tokens > 0 ? (shared_tokens + part_tokens - 1) / part_tokens : 1;
+}
+
+__device__ __forceinline__ SeqUnits seq_units(const PlanInput& in, int s) {
+  SeqUnits u;
+  int n = in.ctx[s];
+  u.n = n < 0 ? 0 : min(n, in.cap);
+  int shared = 0;
+  if (in.group_starts != nullptr) {
+    const int g = group_of(in, s);
+    shared = shared_prefix_tokens(in.group_shared_blocks[g], in.max_shared_blocks,
+                                  in.cap / kBlockTokens);
+  }
+  u.nsp = min(shared_slots(shared, in.part_tokens), in.max_slots);
+  u.base = min(shared, u.n);
+  const int priv = u.n - u.base;
+  const int room = in.max_slots - u.nsp;  // slots left for the private range
+  if (in.part_tokens > 0) {
+    u.full = min(priv / in.part_tokens, room);
+    u.tail_len = priv - u.full * in.part_tokens;
+    u.tail = (u.full < room) && (u.tail_len > 0 || (u.nsp == 0 && u.full == 0));
   } else {
     u.full = 0;
-    u.tail = 1;
-    u.tail_len = n;
+    u.tail_len = priv;
+    u.tail = room > 0 && (priv > 0 || u.nsp == 0);
   }
   return u;
 }
 
+__device__ __forceinline__ int unit_slot(const SeqUnits& u, int p) {
+  const bool only = u.nsp == 0 && u.full + u.tail == 1;
+  return (u.nsp + p) | (only ? kDirectFlag : 0);
+}
+
+// Writes plan entries {sequence, first token, end token, slot | kDirectFlag}, their count,
+// and per sequence the number of partial slots the combine must merge (0: the sequence's
+// only unit writes out / lse itself).
 __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restrict__ plan_count,
-                                           const int32_t* __restrict__ ctx_lens, int batch,
-                                           int cap, int part_tokens, int np, int key_shift) {
+                                           int* __restrict__ nslots, const PlanInput in) {
   __shared__ int s_cursor[kPlanBuckets];
   __shared__ int s_scan[kPlanThreads / kWave];
   __shared__ int s_full_total;
@@ -625,27 +723,35 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
   s_cursor[tid] = 0;
   if (tid == 0) s_full_total = 0;
   __syncthreads();
+  const int P = in.part_tokens;
+  if (in.group_starts != nullptr) {  // groups must tile 0..batch-1 in order
+    for (int g = tid; g < in.num_groups; g += kPlanThreads) {
+      const bool bad = in.group_starts[g] > in.group_starts[g + 1] ||
+                       (g == 0 && in.group_starts[0] != 0) ||
+                       (g == in.num_groups - 1 && in.group_starts[in.num_groups] != in.batch);
+      if (bad) PKV_FLAG_ERROR(PKV_DEVERR_GROUPS);
+    }
+  }
   auto key_of = [&](int len) {
-    return min(kPlanBuckets - 1, ((len + kBlockTokens - 1) / kBlockTokens) >> key_shift);
+    return min(kPlanBuckets - 1, ((len + kBlockTokens - 1) / kBlockTokens) >> in.key_shift);
   };
-  auto n_clamped = [&](int seq) {
-    const int n = ctx_lens[seq];
-    return n < 0 ? 0 : min(n, cap);
-  };
-  for (int base = 0; base < batch; base += kPlanThreads) {
+  for (int base = 0; base < in.batch; base += kPlanThreads) {
     const int s = base + tid;
-    UnitSplit u = {0, 0, 0};
-    if (s < batch) {
-      const int raw = ctx_lens[s];
-      if (raw < 0 || raw > cap) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
-      const int n = n_clamped(s);
-      u = split_units(n, part_tokens, np);
-      if (part_tokens > 0 && n > np * part_tokens) PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
+    SeqUnits u = {0, 0, 0, 0, 0, 0};
+    if (s < in.batch) {
+      const int raw = in.ctx[s];
+      if (raw < 0 || raw > in.cap) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+      u = seq_units(in, s);
+      const int units = u.full + u.tail;
+      const int covered = u.base + u.full * P + (u.tail ? u.tail_len : 0);
+      if (covered < u.n) PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
+      nslots[s] = (u.nsp == 0 && units == 1) ? 0 : u.nsp + units;
       if (u.tail) atomicAdd(&s_cursor[key_of(u.tail_len)], 1);
     }
     const int incl = block_scan_inclusive(s_scan, u.full);
     const int first = s_full_total + incl - u.full;
-    for (int p = 0; p < u.full; ++p) plan[first + p] = make_int4(s, p, n_clamped(s), 0);
+    for (int p = 0; p < u.full; ++p)
+      plan[first + p] = make_int4(s, u.base + p * P, u.base + (p + 1) * P, unit_slot(u, p));
     __syncthreads();
     if (tid == kPlanThreads - 1) s_full_total += incl;
     __syncthreads();
@@ -657,18 +763,21 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
   s_cursor[kb] = s_full_total + incl - h;
   if (tid == kPlanThreads - 1) *plan_count = s_full_total + incl;
   __syncthreads();
-  for (int s = tid; s < batch; s += kPlanThreads) {
-    int n = ctx_lens[s];
-    n = n < 0 ? 0 : min(n, cap);
-    const UnitSplit u = split_units(n, part_tokens, np);
-    if (u.tail) plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] = make_int4(s, u.full, n, 0);
+  for (int s = tid; s < in.batch; s += kPlanThreads) {
+    const SeqUnits u = seq_units(in, s);
+    if (u.tail) {
+      const int t0 = u.base + u.full * P;
+      plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] =
+          make_int4(s, t0, t0 + u.tail_len, unit_slot(u, u.full));
+    }
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    int4* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
-    int batch, int cap, int part_tokens, int np, int key_shift) {
-  build_plan(plan, plan_count, ctx_lens, batch, cap, part_tokens, np, key_shift);
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int4* __restrict__ plan,
+                                                             int* __restrict__ plan_count,
+                                                             int* __restrict__ nslots,
+                                                             const PlanInput in) {
+  build_plan(plan, plan_count, nslots, in);
 }
 
 // Prologue of an append-and-decode step in one launch: workgroup 0 writes the work
@@ -677,20 +786,85 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 constexpr int kAppendPerGroup = kPlanThreads / kWave;
 
 __global__ __launch_bounds__(kPlanThreads) void prologue_kernel(
-    int4* __restrict__ plan, int* __restrict__ plan_count, const int32_t* __restrict__ ctx_lens,
-    int batch, int cap, int part_tokens, int np, int key_shift, uint4* __restrict__ kc,
+    int4* __restrict__ plan, int* __restrict__ plan_count, int* __restrict__ nslots,
+    const PlanInput in, uint4* __restrict__ kc,
     uint4* __restrict__ vc, const uint4* __restrict__ kn, const uint4* __restrict__ vn,
     const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cu, int total, int num_kv_heads, int row_vecs,
     int num_blocks) {
   if (blockIdx.x == 0) {
-    build_plan(plan, plan_count, ctx_lens, batch, cap, part_tokens, np, key_shift);
+    build_plan(plan, plan_count, nslots, in);
     return;
   }
   const int i = (blockIdx.x - 1) * kAppendPerGroup + static_cast<int>(threadIdx.x) / kWave;
   if (i >= total) return;
-  append_token(kc, vc, kn, vn, tables, W, start_pos, cu, batch, total, num_kv_heads, row_vecs,
-               num_blocks, i, static_cast<int>(threadIdx.x) % kWave, &g_pkv_error_word);
+  append_token(kc, vc, kn, vn, tables, W, start_pos, cu, in.batch, total, num_kv_heads,
+               row_vecs, num_blocks, i, static_cast<int>(threadIdx.x) % kWave, &g_pkv_error_word);
+}
+
+// First pass over fork groups' shared prefixes (spindle, "Paging": forks share blocks
+// copy-on-write).  Workgroup = (shared partition, KV head, group); wave w attends for
+// members w, w + kSharedWaves, ... of the group over the group's first
+// group_shared_blocks[g] blocks, writing partial slot `part` of each member.  Every member
+// reads through its own table row, so the result never depends on the sharing being
+// real; for true forks the ids coincide, the sibling waves fetch the same lines, and the
+// plain (cached) loads let HBM serve each shared block once per call.
+constexpr int kSharedWaves = 4;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ group_starts, const int32_t* __restrict__ group_shared_blocks,
+    int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
+    int max_parts, int max_shared_blocks, int batch, float* __restrict__ part_out,
+    float* __restrict__ part_lse) {
+  using Gm = Geom<T, D>;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int g = blockIdx.z;
+  const int shared = shared_prefix_tokens(group_shared_blocks[g], max_shared_blocks, W);
+  const int nsp = min(shared_slots(shared, part_tokens), max_parts);
+  if (part >= nsp) return;
+  const int P = part_tokens > 0 ? part_tokens : shared;
+  const int tok0 = part * P;
+  const int tok1 = min(shared, tok0 + P);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int grp = lane / kLanesPerToken;
+  const int sub = lane % kLanesPerToken;
+  const int cap = W * kBlockTokens;
+  const int m1 = min(group_starts[g + 1], batch);  // malformed groups: stay in range
+  for (int s = max(group_starts[g], 0) + wave; s < m1; s += kSharedWaves) {
+    int n = ctx_lens[s];
+    n = n < 0 ? 0 : min(n, cap);
+    // A member shorter than this slot's start gets an empty range that still begins on
+    // the block boundary tok0 (attend_range needs a block-aligned start).
+    const int t0 = tok0;
+    const int t1 = max(tok0, min(tok1, n));
+    GroupState<T, D, G> st;
+    attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, kvh, num_q_heads,
+                                       num_kv_heads, num_blocks, scale_log2, t0, t1, 0, lane);
+    if (grp == 0) {
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        const float L = st.l[gg];
+        const float ls = L > 0.0f ? (st.m[gg] + __log2f(L)) * kLn2 : -INFINITY;
+        const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + gg;
+        float* dst = part_out + (sh * max_parts + part) * D;
+#pragma unroll
+        for (int e = 0; e < Gm::kElems; e += 4) {
+          float4 v;
+          v.x = L > 0.0f ? st.acc[gg][e + 0] / L : 0.0f;
+          v.y = L > 0.0f ? st.acc[gg][e + 1] / L : 0.0f;
+          v.z = L > 0.0f ? st.acc[gg][e + 2] / L : 0.0f;
+          v.w = L > 0.0f ? st.acc[gg][e + 3] / L : 0.0f;
+          *reinterpret_cast<float4*>(dst + lane_dim<T, D>(sub, e)) = v;
+        }
+        if (sub == 0) part_lse[sh * max_parts + part] = ls;
+      }
+    }
+  }
 }
 
 using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
@@ -729,6 +903,38 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
   pass1_launch<4, 2, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx,
                               hq, hkv, nb, scale_log2, part_tokens, max_parts, part_out,
                               part_lse, out, lse, plan, plan_count);
+}
+
+using SharedFn = void (*)(dim3, hipStream_t, const void*, const void*, const void*,
+                          const int32_t*, int, const int32_t*, const int32_t*, const int32_t*,
+                          int, int, int, float, int, int, int, int, float*, float*);
+
+template <typename T, int D, int G>
+void shared_launch(dim3 grid, hipStream_t stream, const void* q, const void* kc, const void* vc,
+                   const int32_t* tables, int W, const int32_t* ctx, const int32_t* gstart,
+                   const int32_t* gshared, int hq, int hkv, int nb, float scale_log2,
+                   int part_tokens, int max_parts, int max_shared_blocks, int batch,
+                   float* part_out, float* part_lse) {
+  hipLaunchKernelGGL((decode_shared_kernel<T, D, G>), grid, dim3(kSharedWaves * kWave), 0,
+                     stream, static_cast<const T*>(q), static_cast<const T*>(kc),
+                     static_cast<const T*>(vc), tables, W, ctx, gstart, gshared, hq, hkv, nb,
+                     scale_log2, part_tokens, max_parts, max_shared_blocks, batch, part_out,
+                     part_lse);
+}
+
+template <typename T, int D>
+SharedFn pick_shared(int G) {
+  switch (G) {
+    case 1: return shared_launch<T, D, 1>;
+    case 2: return shared_launch<T, D, 2>;
+    case 3: return shared_launch<T, D, 3>;
+    case 4: return shared_launch<T, D, 4>;
+    case 5: return shared_launch<T, D, 5>;
+    case 6: return shared_launch<T, D, 6>;
+    case 7: return shared_launch<T, D, 7>;
+    case 8: return shared_launch<T, D, 8>;
+    default: return nullptr;
+  }
 }
 
 template <typename T, int D>
@@ -780,26 +986,55 @@ float scale_to_log2(float scale) {
   return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
 }
 
-// Workspace: [plan count | plan entries (int4, batch * np) | partial outputs | partial lse].
+// Partitioning of one call.  Plain decode: P = ceil(max_context_len / partition_size)
+// partitions of partition_size tokens when that exceeds one (else one unit per sequence,
+// written straight).  Shared-prefix decode: a sequence's slots are the shared prefix's
+// partitions followed by its private range's, at most P + 1.
+struct Geometry {
+  int tokens;      // partition size used by the units (0: a whole sequence / range)
+  int max_slots;   // partial-result slots per (sequence, query head)
+  bool partials;   // partial-result arrays (and the combine) are needed
+};
+
+Geometry decode_geometry(int32_t max_ctx, int32_t partition_size, bool shared) {
+  const int np = num_partitions(max_ctx, partition_size);
+  Geometry g;
+  if (shared) {
+    g.tokens = partition_size;
+    g.max_slots = (partition_size > 0 ? np : 1) + 1;
+    g.partials = true;
+  } else {
+    const bool split = partition_size > 0 && np > 1;
+    g.tokens = split ? partition_size : 0;
+    g.max_slots = split ? np : 1;
+    g.partials = split;
+  }
+  return g;
+}
+
+// Workspace: [plan count | plan entries (int4, batch * max_slots) | per-sequence slot counts
+// (int32, batch) | partial outputs | partial lse], each part 256-byte aligned.
 struct Workspace {
   int* plan_count = nullptr;
   int4* plan = nullptr;
+  int* nslots = nullptr;
   float* part_out = nullptr;
   float* part_lse = nullptr;
   size_t bytes = 0;
 };
 
-Workspace workspace_layout(void* base, int32_t batch, int32_t hq, int32_t D, int np,
-                           bool partials) {
+Workspace workspace_layout(void* base, int32_t batch, int32_t hq, int32_t D, const Geometry& g) {
   Workspace w;
   char* p = static_cast<char*>(base);
   size_t off = 0;
   w.plan_count = reinterpret_cast<int*>(p + off);
   off += kAlign;
   w.plan = reinterpret_cast<int4*>(p + off);
-  off += align_up(static_cast<size_t>(batch) * np * sizeof(int4));
-  if (partials) {
-    const size_t rows = static_cast<size_t>(batch) * hq * np;
+  off += align_up(static_cast<size_t>(batch) * g.max_slots * sizeof(int4));
+  w.nslots = reinterpret_cast<int*>(p + off);
+  off += align_up(static_cast<size_t>(batch) * sizeof(int));
+  if (g.partials) {
+    const size_t rows = static_cast<size_t>(batch) * hq * g.max_slots;
     w.part_out = reinterpret_cast<float*>(p + off);
     off += align_up(rows * D * sizeof(float));
     w.part_lse = reinterpret_cast<float*>(p + off);
@@ -817,15 +1052,24 @@ int plan_key_shift(int32_t max_context_len, int32_t part_tokens) {
   return shift;
 }
 
-int launch_plan(const Workspace& w, const int32_t* ctx, int32_t batch, int32_t hq, int cap,
-                int tokens, int np, int32_t max_context_len, hipStream_t s) {
-  (void)hq;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, w.plan, w.plan_count, ctx,
-                     batch, cap, tokens, np, plan_key_shift(max_context_len, tokens));
-  return launch_status();
+PlanInput plan_input(const int32_t* ctx, int32_t batch, int cap, const Geometry& g,
+                     int32_t max_context_len, const int32_t* group_starts,
+                     const int32_t* group_shared_blocks, int32_t num_groups,
+                     int32_t max_shared_blocks) {
+  PlanInput in;
+  in.ctx = ctx;
+  in.batch = batch;
+  in.cap = cap;
+  in.part_tokens = g.tokens;
+  in.max_slots = g.max_slots;
+  in.key_shift = plan_key_shift(max_context_len, g.tokens);
+  in.group_starts = group_starts;
+  in.group_shared_blocks = group_shared_blocks;
+  in.num_groups = num_groups;
+  in.max_shared_blocks = max_shared_blocks;
+  return in;
 }
 
-// Shared by the decode entry points: validates, then runs [plan] + pass 1 + [combine].
 struct AppendArgs {
   const void* k_new = nullptr;
   const void* v_new = nullptr;
@@ -834,13 +1078,22 @@ struct AppendArgs {
   int32_t total = 0;
 };
 
+struct Groups {
+  const int32_t* starts = nullptr;         // null: no fork groups
+  const int32_t* shared_blocks = nullptr;
+  int32_t count = 0;
+  int32_t max_shared_blocks = 0;           // host bound of shared_blocks[]
+};
+
+// Shared by the decode entry points: validates, then runs [plan or prologue] +
+// [shared-prefix pass] + first pass + [combine].
 int decode_impl(bool make_plan, float* out, float* lse, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                 size_t workspace_bytes, int32_t dtype, pkv_stream_t stream,
-                const AppendArgs* append = nullptr) {
+                const AppendArgs* append = nullptr, const Groups* groups = nullptr) {
   LaunchFn fn = nullptr;
   int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -848,22 +1101,24 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
   if (st != PKV_OK) return st;
   if (!out) return PKV_ERR_NULL;
   if (batch == 0) return PKV_OK;
-  const int np = num_partitions(max_context_len, partition_size);
-  const bool split = partition_size > 0 && np > 1;
-  const size_t need =
-      pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size);
-  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  const bool shared = groups != nullptr;
+  const Geometry geo = decode_geometry(max_context_len, partition_size, shared);
+  const Workspace need = workspace_layout(nullptr, batch, num_q_heads, head_dim, geo);
+  if (workspace == nullptr || workspace_bytes < need.bytes) return PKV_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_ARG;
-  const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, np, split);
+  const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, geo);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int tokens = split ? partition_size : 0;
   const int cap = static_cast<int>(bt_stride) * kBlockTokens;
+  const PlanInput in = plan_input(context_lens, batch, cap, geo, max_context_len,
+                                  shared ? groups->starts : nullptr,
+                                  shared ? groups->shared_blocks : nullptr,
+                                  shared ? groups->count : 0,
+                                  shared ? groups->max_shared_blocks : 0);
   if (append != nullptr && append->total > 0) {
     const int eb = elem_bytes(dtype);
-    const int groups = 1 + (append->total + kAppendPerGroup - 1) / kAppendPerGroup;
-    hipLaunchKernelGGL(prologue_kernel, dim3(groups), dim3(kPlanThreads), 0, s, w.plan,
-                       w.plan_count, context_lens, batch, cap, tokens, np,
-                       plan_key_shift(max_context_len, tokens),
+    const int wgs = 1 + (append->total + kAppendPerGroup - 1) / kAppendPerGroup;
+    hipLaunchKernelGGL(prologue_kernel, dim3(wgs), dim3(kPlanThreads), 0, s, w.plan,
+                       w.plan_count, w.nslots, in,
                        static_cast<uint4*>(const_cast<void*>(k_cache)),
                        static_cast<uint4*>(const_cast<void*>(v_cache)),
                        static_cast<const uint4*>(append->k_new),
@@ -871,20 +1126,39 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
                        static_cast<int>(bt_stride), append->start_pos, append->cu, append->total,
                        num_kv_heads, head_dim * eb / 16, num_blocks);
     if ((st = launch_status()) != PKV_OK) return st;
-  } else if (make_plan && (st = launch_plan(w, context_lens, batch, num_q_heads, cap, tokens, np,
-                                            max_context_len, s)) != PKV_OK) {
-    return st;
+  } else if (make_plan) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, w.plan, w.plan_count,
+                       w.nslots, in);
+    if ((st = launch_status()) != PKV_OK) return st;
   }
-  fn(kOrderPlanned, np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
+  const float scale_log2 = scale_to_log2(scale);
+  if (shared && groups->count > 0 && groups->max_shared_blocks > 0) {
+    const int shared_tokens =
+        min(groups->max_shared_blocks, static_cast<int>(bt_stride)) * kBlockTokens;
+    const int nsp = min(geo.tokens > 0 ? (shared_tokens + geo.tokens - 1) / geo.tokens : 1,
+                        geo.max_slots);
+    const int G = num_q_heads / num_kv_heads;
+    SharedFn sf = dtype == PKV_F32
+                      ? (head_dim == 64 ? pick_shared<float, 64>(G) : pick_shared<float, 128>(G))
+                      : (head_dim == 64 ? pick_shared<uint16_t, 64>(G)
+                                        : pick_shared<uint16_t, 128>(G));
+    sf(dim3(nsp, num_kv_heads, groups->count), s, q, k_cache, v_cache, block_tables,
+       static_cast<int>(bt_stride), context_lens, groups->starts, groups->shared_blocks,
+       num_q_heads, num_kv_heads, num_blocks, scale_log2, geo.tokens, geo.max_slots,
+       groups->max_shared_blocks, batch, w.part_out, w.part_lse);
+    if ((st = launch_status()) != PKV_OK) return st;
+  }
+  fn(kOrderPlanned, geo.max_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
      static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
-     scale_to_log2(scale), tokens, np, w.part_out, w.part_lse, out, lse, w.plan, w.plan_count);
+     scale_log2, geo.tokens, geo.max_slots, w.part_out, w.part_lse, out, lse, w.plan,
+     w.plan_count);
   if ((st = launch_status()) != PKV_OK) return st;
   // A separate second pass: merging inside the first pass would need device-scope
   // fences (whole-L2 write-back and invalidate per split workgroup), measured to cost
   // far more than this launch.
-  if (split) {
-    combine_launch(s, out, lse, w.part_out, w.part_lse, context_lens, batch, cap, num_q_heads,
-                   head_dim, partition_size, np, 1);
+  if (geo.partials) {
+    combine_launch(s, out, lse, w.part_out, w.part_lse, context_lens, w.nslots, batch, cap,
+                   num_q_heads, head_dim, geo.tokens, geo.max_slots, 1);
     st = launch_status();
   }
   return st;
@@ -899,9 +1173,18 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_context_len,
                                              int32_t partition_size) {
   if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  const int np = num_partitions(max_context_len, partition_size);
-  const bool split = partition_size > 0 && np > 1;
-  return workspace_layout(nullptr, batch, num_q_heads, head_dim, np, split).bytes;
+  return workspace_layout(nullptr, batch, num_q_heads, head_dim,
+                          decode_geometry(max_context_len, partition_size, false))
+      .bytes;
+}
+
+extern "C" size_t pkv_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                                    int32_t head_dim, int32_t max_context_len,
+                                                    int32_t partition_size) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  return workspace_layout(nullptr, batch, num_q_heads, head_dim,
+                          decode_geometry(max_context_len, partition_size, true))
+      .bytes;
 }
 
 extern "C" int pkv_decode_plan(void* workspace, size_t workspace_bytes,
@@ -918,12 +1201,13 @@ extern "C" int pkv_decode_plan(void* workspace, size_t workspace_bytes,
       pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partition_size))
     return PKV_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_ARG;
-  const int np = num_partitions(max_context_len, partition_size);
-  const bool split = partition_size > 0 && np > 1;
-  const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, np, split);
-  return launch_plan(w, context_lens, batch, num_q_heads,
-                     static_cast<int>(bt_stride) * kBlockTokens, split ? partition_size : 0, np,
-                     max_context_len, static_cast<hipStream_t>(stream));
+  const Geometry geo = decode_geometry(max_context_len, partition_size, false);
+  const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, geo);
+  const PlanInput in = plan_input(context_lens, batch, static_cast<int>(bt_stride) * kBlockTokens,
+                                  geo, max_context_len, nullptr, nullptr, 0, 0);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0,
+                     static_cast<hipStream_t>(stream), w.plan, w.plan_count, w.nslots, in);
+  return launch_status();
 }
 
 extern "C" int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
@@ -979,6 +1263,27 @@ extern "C" int pkv_append_paged_decode(
                      stream, &a);
 }
 
+extern "C" int pkv_paged_decode_shared_prefix(
+    float* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* group_shared_blocks, int32_t num_groups,
+    int32_t max_shared_blocks, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+    pkv_stream_t stream) {
+  if (num_groups < 0 || max_shared_blocks < 0 || num_groups > batch) return PKV_ERR_SHAPE;
+  if (batch > 0 && (!group_starts || !group_shared_blocks)) return PKV_ERR_NULL;
+  Groups g;
+  g.starts = group_starts;
+  g.shared_blocks = group_shared_blocks;
+  g.count = num_groups;
+  g.max_shared_blocks = max_shared_blocks;
+  return decode_impl(true, out, lse, q, k_cache, v_cache, block_tables, bt_stride, context_lens,
+                     batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                     stream, nullptr, &g);
+}
+
 extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,
                                          const void* k_cache, const void* v_cache,
                                          const int32_t* block_tables, int64_t bt_stride,
@@ -1003,17 +1308,21 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
   const int4* plan = nullptr;
   const int* plan_count = nullptr;
   int order = kOrderPartMajorReversed;
+  int grid_slots = np;
   if (plan_workspace != nullptr) {
+    // A plan from pkv_decode_plan for the same lengths and partition size: its units
+    // are exactly the partitions (a single-partition plan covers whole sequences, which
+    // is the same range).
     if ((reinterpret_cast<uintptr_t>(plan_workspace) & (kAlign - 1)) != 0) return PKV_ERR_ARG;
+    const Geometry geo = decode_geometry(max_context_len, partition_size, false);
     const Workspace w = workspace_layout(const_cast<void*>(plan_workspace), batch, num_q_heads,
-                                         head_dim, np, false);
+                                         head_dim, geo);
     plan = w.plan;
     plan_count = w.plan_count;
     order = kOrderPlanned;
+    grid_slots = geo.max_slots;
   }
-  // A plan made for one partition covers whole sequences; here every unit is a
-  // partition, so a single-partition plan is only valid when np == 1 as well.
-  fn(order, np, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
+  fn(order, grid_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
      static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
      scale_to_log2(scale), partition_size, max_partitions, part_out, part_lse, nullptr, nullptr,
      plan, plan_count);
@@ -1033,6 +1342,6 @@ extern "C" int pkv_lse_combine(float* out, float* lse, const float* part_out,
   const int64_t cap64 = static_cast<int64_t>(max_partitions) * partition_size;
   const int cap = cap64 > (1 << 30) ? (1 << 30) : static_cast<int>(cap64);
   combine_launch(static_cast<hipStream_t>(stream), out, lse, part_out, part_lse, context_lens,
-                 batch, cap, num_q_heads, head_dim, partition_size, max_partitions, 0);
+                 nullptr, batch, cap, num_q_heads, head_dim, partition_size, max_partitions, 0);
   return launch_status();
 }

@@ -215,6 +215,38 @@ def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_p
     return out, lse
 
 
+def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                               group_shared_blocks, max_shared_blocks, max_context_len,
+                               scale=None, partition_size=0, out=None, lse=None, workspace=None,
+                               want_lse=True, stream=None):
+    """Decode a batch of copy-on-write fork groups, streaming each group's shared
+    leading blocks once for all members (see pkv_paged_decode_shared_prefix)."""
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    _gpu(group_starts, "group_starts", torch.int32)
+    _gpu(group_shared_blocks, "group_shared_blocks", torch.int32)
+    G = group_shared_blocks.shape[0]
+    if group_starts.shape != (G + 1,):
+        raise ValueError("group_starts must have num_groups + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    _gpu(out, "out", torch.float32)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+    need = int(_lib.lib().pkv_shared_prefix_workspace_bytes(B, hq, d, int(max_context_len),
+                                                            int(partition_size)))
+    workspace, wbytes = _workspace(workspace, need, q.device)
+    _lib.call("pkv_paged_decode_shared_prefix", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
+              _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+              _ptr(group_starts), _ptr(group_shared_blocks), G, int(max_shared_blocks), B, hq,
+              hkv, d, BLOCK_SIZE, nb, int(max_context_len), float(scale), int(partition_size),
+              _ptr(workspace), wbytes, _kv_code(k_cache), _stream(stream))
+    return out, lse
+
+
 def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                           partition_size, scale=None, max_partitions=None, part_out=None,
                           part_lse=None, plan_workspace=None, stream=None):

@@ -336,8 +336,10 @@ def test_partials_with_and_without_plan_identical():
 
 @pytest.mark.parametrize("P", [0, 64, 1024])
 def test_plan_lists_every_unit_once_longest_first(P):
-    """Plan layout inside the workspace: int32 count at byte 0, int4 (seq, partition,
-    context length, 0) entries from byte 256."""
+    """Plan layout inside the workspace: int32 count at byte 0; from byte 256 int4
+    entries (sequence, first token, end token, slot | 1<<30 when the unit is the
+    sequence's only one and writes the output itself); then one int32 per sequence,
+    the number of slots the combine merges (0 for a direct sequence)."""
     lens = [0, 1, 15, 16, 17, 64, 65, 130, 1024, 1025, 3000, 5, 700, 64]
     case = build_case("plan", lens, 8, 2, 64, "bf16", seed=3)
     dc = DeviceCase(case)
@@ -345,17 +347,28 @@ def test_plan_lists_every_unit_once_longest_first(P):
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     count = int(raw[:4].view(np.int32)[0])
-    full = raw[256:256 + 16 * count].view(np.int32).reshape(-1, 4)
-    assert all(int(n) == lens[int(s_)] for s_, _, n, _ in full.tolist())
-    ent = full[:, :2]
-    want = []
-    for s, n in enumerate(lens):
-        np_ = 1 if P == 0 else max(1, -(-n // P))
-        want += [(s, p) for p in range(np_)]
-    assert count == len(want)
-    assert sorted(map(tuple, ent.tolist())) == sorted(want)
-    size = [min(P, lens[s] - p * P) if P else lens[s] for s, p in ent.tolist()]
-    blocks = [-(-x // 16) for x in size]
+    split = P > 0 and dc.max_ctx > P
+    max_slots = -(-dc.max_ctx // P) if split else 1
+    ent = raw[256:256 + 16 * count].view(np.int32).reshape(-1, 4).tolist()
+    off = 256 + -(-len(lens) * max_slots * 16 // 256) * 256
+    nslots = raw[off:off + 4 * len(lens)].view(np.int32).tolist()
+    direct = 1 << 30
+    per_seq = {}
+    for s_, t0, t1, w in ent:
+        per_seq.setdefault(s_, []).append((t0, t1, w))
+    assert sorted(per_seq) == list(range(len(lens)))
+    for s_, n in enumerate(lens):
+        units = sorted(per_seq[s_])
+        want = [(p * P, min((p + 1) * P, n)) for p in range(max(1, -(-n // P)))] \
+            if split else [(0, n)]
+        assert [(t0, t1) for t0, t1, _ in units] == want, s_
+        if len(want) == 1:
+            assert units[0][2] == direct and nslots[s_] == 0, s_
+        else:
+            assert [w for _, _, w in units] == list(range(len(want))), s_
+            assert nslots[s_] == len(want), s_
+    assert count == sum(len(v) for v in per_seq.values())
+    blocks = [-(-(t1 - t0) // 16) for _, t0, t1, _ in ent]
     assert blocks == sorted(blocks, reverse=True), "plan is not longest-first"
     assert_no_device_error()
 

@@ -254,9 +254,16 @@ def fork_case(name, prefix_lens, forks_per_parent, private_lens, num_q_heads, nu
     st = streams or _streams(seed)
     prefix_lens = [int(x) for x in prefix_lens]
     P = len(prefix_lens)
-    private_lens = np.asarray(private_lens, np.int64).reshape(P, forks_per_parent)
+    if np.ndim(forks_per_parent) == 0:
+        forks = [int(forks_per_parent)] * P
+        private_lens = np.asarray(private_lens, np.int64).reshape(P, forks[0]).tolist()
+    else:  # one fork count per parent, private_lens ragged to match
+        forks = [int(f) for f in forks_per_parent]
+        private_lens = [[int(x) for x in row] for row in private_lens]
+        if [len(r) for r in private_lens] != forks:
+            raise ValueError("private_lens rows must match forks_per_parent")
     for p in range(P):
-        if prefix_lens[p] % block_size and (private_lens[p] > 0).any():
+        if prefix_lens[p] % block_size and any(x > 0 for x in private_lens[p]):
             raise ValueError("unaligned prefix with private tokens needs a CoW copy")
     pref_nb = [-(-n // block_size) for n in prefix_lens]
     priv_nb = [[-(-int(x) // block_size) for x in row] for row in private_lens]
@@ -271,16 +278,16 @@ def fork_case(name, prefix_lens, forks_per_parent, private_lens, num_q_heads, nu
         pos += nb
     rows, ctx, parent = [], [], []
     for p in range(P):
-        for f in range(forks_per_parent):
+        for f in range(forks[p]):
             rows.append((prefix_ids[p], priv_nb[p][f]))
-            ctx.append(prefix_lens[p] + int(private_lens[p, f]))
+            ctx.append(prefix_lens[p] + int(private_lens[p][f]))
             parent.append(p)
     tables, poison, unused = _layout(rows, order[pos:], None, block_size)
     ctx = np.asarray(ctx, np.int32)
     case = _fill(name, ctx, tables, num_blocks, poison, unused, num_q_heads, num_kv_heads,
                  head_dim, kv_dtype, 1, st, 1.0, block_size,
                  fork_parent=np.asarray(parent, np.int32),
-                 shared_blocks=sum(pref_nb) if forks_per_parent > 1 else 0)
+                 shared_blocks=sum(nb for nb, f in zip(pref_nb, forks) if f > 1))
     return case
 
 
