@@ -51,6 +51,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time for the oracle baseline (repeats the whole batch)")
     p.add_argument("--no-copy-probe", action="store_true")
+    p.add_argument("--no-shared-prefix", action="store_true",
+                   help="decode fork workloads with the plain path (each fork re-reads the "
+                        "shared prefix) instead of the shared-prefix path")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="before the timed steps, run 3 device copies of MIB MiB (a known-size "
                         "reference for HBM traffic counters)")
@@ -252,7 +255,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import paged_kv_cache_200_amd as pkv
-    from workloads import bf16_bits, config_case, parallel_normal
+    from workloads import bf16_bits, block_refcounts, config_case, fork_groups, parallel_normal
 
     if args.workload == "gpt2_replay":
         print(json.dumps(run_replay(args, np, torch, pkv)), flush=True)
@@ -285,21 +288,50 @@ def main():
     if case.kv_dtype == "bf16":
         kn, vn = bf16_bits(kn), bf16_bits(vn)
     k_new, v_new = to_dev(kn), to_dev(vn)
-    start = to_dev((case.context_lens - 1).clip(min=0).astype(np.int32))
-    cu = to_dev(np.arange(B + 1, dtype=np.int32))
+    start_np = (case.context_lens - 1).clip(min=0).astype(np.int32)
+    counts = (case.context_lens > 0).astype(np.int32)
+    if case.shared_blocks:
+        # copy-on-write: a token is never written into a block that several sequences
+        # hold (a fork with no private token would first get its own copy)
+        refs = block_refcounts(case)
+        for s_ in range(B):
+            if counts[s_] and refs[int(case.block_tables[s_, start_np[s_] // 16])] > 1:
+                counts[s_] = 0
+    start = to_dev(start_np)
+    cu = to_dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    total_new = int(counts.sum())
+    kn, vn = kn[counts > 0], vn[counts > 0]
+    k_new, v_new = to_dev(kn), to_dev(vn)
     out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
-    ws_bytes = pkv.decode_workspace_bytes(B, hq, d, max_ctx, P)
+    shared_path = case.fork_parent is not None and not args.no_shared_prefix
+    if shared_path:
+        gs_np, gb_np = fork_groups(case)
+        gstarts, gblocks, max_shared = to_dev(gs_np), to_dev(gb_np), int(gb_np.max())
+        ws_bytes = pkv.shared_prefix_workspace_bytes(B, hq, d, max_ctx, P)
+    else:
+        ws_bytes = pkv.decode_workspace_bytes(B, hq, d, max_ctx, P)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     scale = float(case.scale)
 
+    def shared_decode(l):
+        pkv.paged_decode_shared_prefix(qs[l], kcs[l], vcs[l], tables, ctx, gstarts, gblocks,
+                                       max_shared, max_ctx, scale=scale, partition_size=P,
+                                       out=out, lse=lse, workspace=ws)
+
     def step():
-        # per layer: kv_append + paged_decode in one library call (append and work plan
-        # share a launch)
         for l in range(layers):
-            pkv.append_paged_decode(qs[l], kcs[l], vcs[l], k_new, v_new, tables, start, cu, ctx,
-                                    max_ctx, scale=scale, partition_size=P, out=out, lse=lse,
-                                    workspace=ws)
+            if shared_path:
+                # fork groups: append, then one decode call that streams each group's
+                # shared blocks once for all members
+                pkv.kv_append(kcs[l], vcs[l], k_new, v_new, tables, start, cu)
+                shared_decode(l)
+            else:
+                # kv_append + paged_decode in one library call (append and work plan
+                # share a launch)
+                pkv.append_paged_decode(qs[l], kcs[l], vcs[l], k_new, v_new, tables, start,
+                                        cu, ctx, max_ctx, scale=scale, partition_size=P,
+                                        out=out, lse=lse, workspace=ws)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -339,7 +371,15 @@ def main():
     # split, else the planned decode, which is then that single launch
     np_max = max(1, -(-max_ctx // P)) if P > 0 else 1
     plan_ws = pkv.decode_plan(ctx, tables, hq, d, max_ctx, P)
-    if np_max > 1:
+    timed_kernel = "decode_pass1_kernel"
+    if shared_path:
+        # no single dominant kernel: the whole decode call (plan, shared-prefix pass, first
+        # pass over the private ranges, combine) against the unique bytes
+        timed_kernel = "paged_decode_shared_prefix call"
+
+        def pass1():
+            shared_decode(0)
+    elif np_max > 1:
         part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
         part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
 
@@ -366,7 +406,7 @@ def main():
     if flags:
         raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
 
-    decode_bytes, append_bytes = algorithmic_bytes(case, B)
+    decode_bytes, append_bytes = algorithmic_bytes(case, total_new)
     # shared (copy-on-write) blocks need to come from HBM once per call
     logical_tokens = int(case.context_lens.sum())
     unique_tokens = unique_kv_tokens(case) if case.shared_blocks else logical_tokens
@@ -412,7 +452,11 @@ def main():
             "num_blocks": case.num_blocks,
             "layers": layers,
             "partition_size": P,
-            "step": "append 1 token/seq + work plan (one launch), split-KV first pass, LSE combine",
+            "step": ("append + shared-prefix decode (plan, shared pass, first pass, combine)"
+                     if shared_path else
+                     "append 1 token/seq + work plan (one launch), split-KV first pass, "
+                     "LSE combine"),
+            "appended_tokens_per_layer": total_new,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_ctx / step_s, 1),
@@ -421,7 +465,7 @@ def main():
         "logical_kv_bytes_per_layer": logical_tokens * kv_tok,
         "unique_kv_bytes_per_layer": unique_tokens * kv_tok,
         "roofline": {
-            "kernel": "decode_pass1_kernel",
+            "kernel": timed_kernel,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

@@ -803,14 +803,74 @@ __global__ __launch_bounds__(kPlanThreads) void prologue_kernel(
 }
 
 // First pass over fork groups' shared prefixes (spindle, "Paging": forks share blocks
-// copy-on-write).  Workgroup = (shared partition, KV head, group); wave w attends for
-// members w, w + kSharedWaves, ... of the group over the group's first
-// group_shared_blocks[g] blocks, writing partial slot `part` of each member.  Every member
-// reads through its own table row, so the result never depends on the sharing being
-// real; for true forks the ids coincide, the sibling waves fetch the same lines, and the
-// plain (cached) loads let HBM serve each shared block once per call.
+// copy-on-write).  Workgroup = (shared partition, KV head, group).  Partition `part`
+// covers shared tokens [part * P, min((part + 1) * P, shared)); every member of the group
+// gets its partial result for that range in slot `part`, the plan puts its private range
+// in the slots after the shared ones, and the combine merges them.
 constexpr int kSharedWaves = 4;
 
+// Slot `part` of member s over shared tokens [tok0, tok1) by one wave, through the
+// member's own table row (plain loads, so sibling waves find the blocks cached).
+template <typename T, int D, int G>
+__device__ __forceinline__ void shared_member(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ tables, int W, int s, int n, int kvh, int num_q_heads,
+    int num_kv_heads, int num_blocks, float scale_log2, int tok0, int tok1, int part,
+    int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse, int lane) {
+  using Gm = Geom<T, D>;
+  const int grp = lane / kLanesPerToken;
+  const int sub = lane % kLanesPerToken;
+  // A member shorter than this slot's start gets an empty range that still begins on
+  // the block boundary tok0 (attend_range needs a block-aligned start).
+  const int t1 = max(tok0, min(tok1, n));
+  GroupState<T, D, G> st;
+  attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, kvh, num_q_heads,
+                                     num_kv_heads, num_blocks, scale_log2, tok0, t1, 0, lane);
+  if (grp != 0) return;
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float L = st.l[gg];
+    const float ls = L > 0.0f ? (st.m[gg] + __log2f(L)) * kLn2 : -INFINITY;
+    const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + gg;
+    float* dst = part_out + (sh * max_parts + part) * D;
+#pragma unroll
+    for (int e = 0; e < Gm::kElems; e += 4) {
+      float4 v;
+      v.x = L > 0.0f ? st.acc[gg][e + 0] / L : 0.0f;
+      v.y = L > 0.0f ? st.acc[gg][e + 1] / L : 0.0f;
+      v.z = L > 0.0f ? st.acc[gg][e + 2] / L : 0.0f;
+      v.w = L > 0.0f ? st.acc[gg][e + 3] / L : 0.0f;
+      *reinterpret_cast<float4*>(dst + lane_dim<T, D>(sub, e)) = v;
+    }
+    if (sub == 0) part_lse[sh * max_parts + part] = ls;
+  }
+}
+
+struct SharedRange {
+  int tok0, tok1;  // shared tokens of this workgroup's slot
+  int m0, m1;      // the group's members, clamped to [0, batch)
+  bool live;
+};
+
+__device__ __forceinline__ SharedRange shared_range(const int32_t* __restrict__ group_starts,
+                                                    const int32_t* __restrict__ group_shared,
+                                                    int g, int part, int part_tokens,
+                                                    int max_parts, int max_shared_blocks, int W,
+                                                    int batch) {
+  SharedRange r;
+  const int shared = shared_prefix_tokens(group_shared[g], max_shared_blocks, W);
+  const int nsp = min(shared_slots(shared, part_tokens), max_parts);
+  r.live = part < nsp;
+  const int P = part_tokens > 0 ? part_tokens : shared;
+  r.tok0 = part * P;
+  r.tok1 = min(shared, r.tok0 + P);
+  r.m0 = max(group_starts[g], 0);  // malformed groups (flagged by the plan): stay in range
+  r.m1 = min(group_starts[g + 1], batch);
+  return r;
+}
+
+// Generic version: wave w attends for members w, w + kSharedWaves, ..., each through its
+// own table row.  Sibling waves fetch the same blocks, so HBM serves most of them once.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -819,50 +879,369 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(
     int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
     int max_parts, int max_shared_blocks, int batch, float* __restrict__ part_out,
     float* __restrict__ part_lse) {
-  using Gm = Geom<T, D>;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int g = blockIdx.z;
-  const int shared = shared_prefix_tokens(group_shared_blocks[g], max_shared_blocks, W);
-  const int nsp = min(shared_slots(shared, part_tokens), max_parts);
-  if (part >= nsp) return;
-  const int P = part_tokens > 0 ? part_tokens : shared;
-  const int tok0 = part * P;
-  const int tok1 = min(shared, tok0 + P);
+  const SharedRange r = shared_range(group_starts, group_shared_blocks, blockIdx.z, blockIdx.x,
+                                     part_tokens, max_parts, max_shared_blocks, W, batch);
+  if (!r.live) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  const int grp = lane / kLanesPerToken;
-  const int sub = lane % kLanesPerToken;
   const int cap = W * kBlockTokens;
-  const int m1 = min(group_starts[g + 1], batch);  // malformed groups: stay in range
-  for (int s = max(group_starts[g], 0) + wave; s < m1; s += kSharedWaves) {
+  for (int s = r.m0 + wave; s < r.m1; s += kSharedWaves) {
     int n = ctx_lens[s];
     n = n < 0 ? 0 : min(n, cap);
-    // A member shorter than this slot's start gets an empty range that still begins on
-    // the block boundary tok0 (attend_range needs a block-aligned start).
-    const int t0 = tok0;
-    const int t1 = max(tok0, min(tok1, n));
-    GroupState<T, D, G> st;
-    attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, kvh, num_q_heads,
-                                       num_kv_heads, num_blocks, scale_log2, t0, t1, 0, lane);
-    if (grp == 0) {
+    shared_member<T, D, G>(q, kc, vc, tables, W, s, n, blockIdx.y, num_q_heads, num_kv_heads,
+                           num_blocks, scale_log2, r.tok0, r.tok1, blockIdx.x, max_parts,
+                           part_out, part_lse, lane);
+  }
+}
+
+// Matrix-core version (bf16 cache).  The group's query rows, (member, query head) pairs,
+// 16 per tile, are attended together against each shared block, which is read once per
+// tile through the first member's table row: 16 x 16 score tiles S^T = K Q^T on the bf16
+// MFMA (16x16x32), then O += P V on the fp32 MFMA (16x16x4), so the probabilities enter
+// the product unrounded.  Four waves take the range's blocks round-robin, each with its
+// own online softmax per row, and are merged through LDS.  A member whose table row does
+// not hold the same block ids over its share of the range is attended separately through
+// its own row, so the result never depends on the sharing being real.
+//
+// Lane layouts (c = lane % 16, h = lane / 16):
+//   S^T tile: lane holds rows c, tokens 4h + r (r = 0..3) of the block.  The score
+//     contraction runs over dims permuted so that lane h-group loads one contiguous D/4
+//     run: K[token c][h * D/4 + 8k ..] and Q[row c][h * D/4 + 8k ..].
+//   P V step k (k = 0..3): A = P[row c][token 4h + k] (the lane's own score r = k),
+//     B = V[token 4h + k][c * D/16 + j] for output tile j, so lane loads the D/16
+//     contiguous dims c * D/16 .. of 4 tokens.
+//   O tile j: lane holds rows 4h + r, dim c * D/16 + j.
+constexpr int kMfmaRows = 16;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct MfmaGeom {
+  static constexpr int kQkSteps = D / 32;   // 16x16x32 steps over the head dim
+  static constexpr int kRun = D / 4;        // contiguous dims per lane in the score step
+  static constexpr int kTiles = D / 16;     // output tiles of 16 dims
+  static constexpr int kVWords = D / 32;    // 32-bit words of V per lane and token
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+};
+
+template <int D>
+struct MfmaBlock {
+  u32x4_t k[MfmaGeom<D>::kQkSteps];
+  uint32_t v[4][MfmaGeom<D>::kVWords];
+};
+
+template <int D>
+__device__ __forceinline__ void mfma_load_block(MfmaBlock<D>& b, const uint16_t* __restrict__ kt,
+                                                const uint16_t* __restrict__ vt, int c, int h) {
+  using Mg = MfmaGeom<D>;
 #pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const float L = st.l[gg];
-        const float ls = L > 0.0f ? (st.m[gg] + __log2f(L)) * kLn2 : -INFINITY;
-        const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + gg;
-        float* dst = part_out + (sh * max_parts + part) * D;
+  for (int k = 0; k < Mg::kQkSteps; ++k)
+    b.k[k] = *reinterpret_cast<const u32x4_t*>(kt + c * D + h * Mg::kRun + 8 * k);
 #pragma unroll
-        for (int e = 0; e < Gm::kElems; e += 4) {
-          float4 v;
-          v.x = L > 0.0f ? st.acc[gg][e + 0] / L : 0.0f;
-          v.y = L > 0.0f ? st.acc[gg][e + 1] / L : 0.0f;
-          v.z = L > 0.0f ? st.acc[gg][e + 2] / L : 0.0f;
-          v.w = L > 0.0f ? st.acc[gg][e + 3] / L : 0.0f;
-          *reinterpret_cast<float4*>(dst + lane_dim<T, D>(sub, e)) = v;
-        }
-        if (sub == 0) part_lse[sh * max_parts + part] = ls;
+  for (int k = 0; k < 4; ++k) {
+    const uint16_t* src = vt + (4 * h + k) * D + c * Mg::kTiles;
+    if constexpr (Mg::kVWords == 4) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.v[k][j] = w[j];
+    } else {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
+      b.v[k][0] = w[0];
+      b.v[k][1] = w[1];
+    }
+  }
+}
+
+// LDS of one row tile: per member its token limit and whether its table row matches the
+// tile leader's; per wave and row the softmax state and the unnormalised output.
+template <int D>
+struct MfmaShared {
+  int n[kMfmaRows];
+  int mismatch[kMfmaRows];
+  float m[kSharedWaves][kMfmaRows];
+  float l[kSharedWaves][kMfmaRows];
+  float4 o[kSharedWaves][kMfmaRows][D / 4];
+};
+
+// Rows of the members selected by `take` (bit mi: member base + mi), attended over
+// tokens [tok0, sm.n[mi]) through table row `lead`; row (s, h) is written to
+// dst_out[(s * Hq + h) * slots + slot] (D floats) and dst_lse[...] (nullable).  Called by
+// all threads of the workgroup (it synchronises).
+template <int D, int G>
+__device__ __forceinline__ void mfma_tile(
+    MfmaShared<D>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ lead, int base,
+    unsigned take, int kvh, int num_q_heads, int num_kv_heads, int num_blocks,
+    float scale_log2, int tok0, int slot, int slots, float* __restrict__ dst_out,
+    float* __restrict__ dst_lse) {
+  using Mg = MfmaGeom<D>;
+  constexpr int kMembers = kMfmaRows / G;
+  constexpr int kRows = kMembers * G;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int c = lane % 16;
+  const int h = lane / 16;
+  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
+  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
+  const int b0 = tok0 / kBlockTokens;
+
+  int n_max = 0;
+#pragma unroll
+  for (int mi = 0; mi < kMembers; ++mi)
+    if ((take >> mi) & 1u) n_max = max(n_max, sm.n[mi]);
+  const bool c_live = c < kRows && ((take >> (c / G)) & 1u);
+  const int n_c = c_live ? sm.n[c / G] : 0;
+
+  // Query rows as the B operand of the score step (zero for rows not taken).
+  u32x4_t qr[Mg::kQkSteps];
+#pragma unroll
+  for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = u32x4_t{0u, 0u, 0u, 0u};
+  if (c_live) {
+    const uint16_t* qrow =
+        q + (static_cast<size_t>(base + c / G) * num_q_heads + kvh * G + c % G) * D + h * Mg::kRun;
+#pragma unroll
+    for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * k);
+  }
+
+  float m_c = -INFINITY;  // running max of row c, log2 units (lazy, as in the first pass)
+  float l_part = 0.0f;    // this lane's share of row c's exp-sum
+  f32x4_t o[Mg::kTiles];
+#pragma unroll
+  for (int j = 0; j < Mg::kTiles; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nblk = n_max > tok0 ? (n_max - tok0 + kBlockTokens - 1) / kBlockTokens : 0;
+  const int nw = nblk > wave ? (nblk - wave + kSharedWaves - 1) / kSharedWaves : 0;
+  // Block ids of this wave's blocks, 64 at a time, one per lane.
+  int id_base = 0;
+  auto fetch_ids = [&](int from) -> int {
+    const int k = from + lane;
+    int id = 0;
+    bool bad = false;
+    if (k < nw) {
+      id = lead[b0 + wave + kSharedWaves * k];
+      bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
+      id = bad ? 0 : id;
+    }
+    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+    return id;
+  };
+  int ids = fetch_ids(0);
+  auto load = [&](MfmaBlock<D>& bl, int k) {  // called with k = 0, 1, 2, ... in order
+    if (k - id_base >= kWave) {
+      id_base += kWave;
+      ids = fetch_ids(id_base);
+    }
+    const int id = __builtin_amdgcn_readlane(ids, k - id_base);
+    const size_t off = static_cast<size_t>(id) * block_elems + kvh * head_elems;
+    mfma_load_block<D>(bl, kc + off, vc + off, c, h);
+  };
+  auto process = [&](const MfmaBlock<D>& cur, int k) {
+    const int t_base = (b0 + wave + kSharedWaves * k) * kBlockTokens;  // token of slot 0
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < Mg::kQkSteps; ++s)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
+                                                   __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
+                                                   0);
+    // Scores of row c for tokens 4h + i, masked by the row's own length (select, so
+    // stale or NaN slots never pass).
+    float x[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, x[i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const bool raise = bm > m_c + kLazyMaxSlack;
+    if (__any(raise)) {
+      float a = 1.0f;
+      if (raise) {
+        a = m_c == -INFINITY ? 0.0f : fast_exp2(m_c - bm);
+        m_c = bm;
       }
+      l_part *= a;
+      // Output rows 4h + i take the factor of the lanes that own score row 4h + i.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(a, 4 * h + i);
+#pragma unroll
+        for (int j = 0; j < Mg::kTiles; ++j) o[j][i] *= ai;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - m_c);
+      l_part += p[i];
+    }
+    // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
+    const bool tail = t_base + kBlockTokens > n_max;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool vok = !tail || (t_base + 4 * h + i < n_max);
+#pragma unroll
+      for (int w = 0; w < Mg::kVWords; ++w) {
+        const uint32_t bits = vok ? cur.v[i][w] : 0u;
+        o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], bf16_lo(bits), o[2 * w], 0, 0, 0);
+        o[2 * w + 1] =
+            __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], bf16_hi(bits), o[2 * w + 1], 0, 0, 0);
+      }
+    }
+  };
+  // Two blocks in flight: the next block's loads are issued before this one's math.
+  MfmaBlock<D> bufa, bufb;
+  if (nw > 0) load(bufa, 0);
+  for (int k = 0; k < nw; k += 2) {
+    if (k + 1 < nw) load(bufb, k + 1);
+    process(bufa, k);
+    if (k + 1 < nw) {
+      if (k + 2 < nw) load(bufa, k + 2);
+      process(bufb, k + 1);
+    }
+  }
+  float l_c = l_part;
+  l_c += __shfl_xor(l_c, 16);
+  l_c += __shfl_xor(l_c, 32);
+
+  // Merge the waves: each publishes (m, l) per row and its unnormalised rows.
+  constexpr int kQuads = Mg::kTiles / 4;  // float4s per lane and row
+  if (h == 0) {
+    sm.m[wave][c] = m_c;
+    sm.l[wave][c] = l_c;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u)
+      sm.o[wave][4 * h + i][c * kQuads + u] =
+          make_float4(o[4 * u][i], o[4 * u + 1][i], o[4 * u + 2][i], o[4 * u + 3][i]);
+  }
+  __syncthreads();
+  const int row = tid / 16;  // 16 rows x 16 threads of D/16 dims
+  const int cc = tid % 16;
+  const int mi = row / G;
+  if (row < kRows && ((take >> mi) & 1u)) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSharedWaves; ++w) M = fmaxf(M, sm.m[w][row]);
+    float e[kSharedWaves];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSharedWaves; ++w) {
+      e[w] = sm.m[w][row] == -INFINITY ? 0.0f : fast_exp2(sm.m[w][row] - M);
+      L += sm.l[w][row] * e[w];
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const size_t sh = static_cast<size_t>(base + mi) * num_q_heads + kvh * G + row % G;
+    float* dst = dst_out + (sh * slots + slot) * D + cc * Mg::kTiles;
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int w = 0; w < kSharedWaves; ++w) {
+        const float4 x = sm.o[w][row][cc * kQuads + u];
+        acc.x = fmaf(e[w], x.x, acc.x);
+        acc.y = fmaf(e[w], x.y, acc.y);
+        acc.z = fmaf(e[w], x.z, acc.z);
+        acc.w = fmaf(e[w], x.w, acc.w);
+      }
+      acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
+      // dims cc * D/16 + j of tile j: float4 u holds tiles 4u .. 4u + 3
+      *reinterpret_cast<float4*>(dst + 4 * u) = acc;
+    }
+    if (cc == 0 && dst_lse != nullptr)
+      dst_lse[sh * slots + slot] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();  // LDS reused by the next call
+}
+
+// One launch for a batch of fork groups: workgroups [0, shared_wgs) are (shared partition,
+// KV head, group) = (x % nsp, x / nsp % Hkv, x / (nsp * Hkv)); the rest take the plan's
+// units (each sequence's private range, and whole sequences of groups that share nothing),
+// unit (x - shared_wgs) / Hkv for KV head (x - shared_wgs) % Hkv, as one-member tiles
+// through the member's own table row.  The private units' short latency chains overlap
+// the shared stream instead of following it.
+template <int D, int G>
+__global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ group_starts,
+    const int32_t* __restrict__ group_shared_blocks, int num_groups, int nsp_grid,
+    int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
+    int max_parts, int max_shared_blocks, int batch, float* __restrict__ part_out,
+    float* __restrict__ part_lse, float* __restrict__ out, float* __restrict__ lse,
+    const int4* __restrict__ plan, const int* __restrict__ plan_count) {
+  constexpr int kMembers = kMfmaRows / G;  // members per row tile
+  __shared__ MfmaShared<D> sm;
+  const int tid = threadIdx.x;
+  const int cap = W * kBlockTokens;
+  const int shared_wgs = nsp_grid * num_kv_heads * num_groups;
+  const int x = blockIdx.x;
+  if (x >= shared_wgs) {
+    const int u = (x - shared_wgs) / num_kv_heads;
+    const int kvh = (x - shared_wgs) % num_kv_heads;
+    if (u >= *plan_count) return;
+    const int4 e = plan[u];
+    const int s = e.x;
+    const int slot = e.w & kSlotMask;
+    const bool direct = (e.w & kDirectFlag) != 0;
+    if (tid == 0) {
+      int n = ctx_lens[s];
+      n = n < 0 ? 0 : min(n, cap);
+      sm.n[0] = min(n, e.z);
+    }
+    __syncthreads();
+    mfma_tile<D, G>(sm, q, kc, vc, tables + static_cast<size_t>(s) * W, s, 1u, kvh, num_q_heads,
+                    num_kv_heads, num_blocks, scale_log2, e.y, direct ? 0 : slot,
+                    direct ? 1 : max_parts, direct ? out : part_out, direct ? lse : part_lse);
+    return;
+  }
+  const int part = x % nsp_grid;
+  const int kvh = (x / nsp_grid) % num_kv_heads;
+  const SharedRange r = shared_range(group_starts, group_shared_blocks, x / (nsp_grid * num_kv_heads),
+                                     part, part_tokens, max_parts, max_shared_blocks, W, batch);
+  if (!r.live) return;
+  const int b0 = r.tok0 / kBlockTokens;
+  const int span = (r.tok1 - r.tok0 + kBlockTokens - 1) / kBlockTokens;
+  for (int base = r.m0; base < r.m1; base += kMembers) {
+    const int cnt = min(kMembers, r.m1 - base);
+    if (tid < kMembers) {
+      int n = tid < cnt ? ctx_lens[base + tid] : 0;
+      n = n < 0 ? 0 : min(n, cap);
+      sm.n[tid] = min(n, r.tok1);
+      sm.mismatch[tid] = 0;
+    }
+    __syncthreads();
+    // Compare each member's block ids over its share of the range with the tile leader's.
+    const int32_t* lead = tables + static_cast<size_t>(base) * W;
+    for (int i = tid; i < cnt * span; i += kSharedWaves * kWave) {
+      const int mi = i / span;
+      const int b = b0 + i % span;
+      if (b * kBlockTokens < sm.n[mi] && tables[static_cast<size_t>(base + mi) * W + b] != lead[b])
+        sm.mismatch[mi] = 1;
+    }
+    __syncthreads();
+    unsigned shared_take = 0;
+    for (int mi = 0; mi < cnt; ++mi) shared_take |= sm.mismatch[mi] ? 0u : (1u << mi);
+    // Pass 0: the members that share, through the leader's row.  Then one pass per member
+    // whose ids differ (the sharing hint was wrong), through its own row.
+    unsigned pending = ~shared_take & ((1u << cnt) - 1u);
+    for (int pass = 0; pass == 0 || pending != 0; ++pass) {
+      unsigned take = shared_take;
+      const int32_t* row = lead;
+      if (pass > 0) {
+        const int mi = __builtin_ctz(pending);
+        pending &= pending - 1u;
+        take = 1u << mi;
+        row = tables + static_cast<size_t>(base + mi) * W;
+      }
+      mfma_tile<D, G>(sm, q, kc, vc, row, base, take, kvh, num_q_heads, num_kv_heads,
+                      num_blocks, scale_log2, r.tok0, part, max_parts, part_out, part_lse);
     }
   }
 }
@@ -905,21 +1284,56 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
                               part_lse, out, lse, plan, plan_count);
 }
 
-using SharedFn = void (*)(dim3, hipStream_t, const void*, const void*, const void*,
-                          const int32_t*, int, const int32_t*, const int32_t*, const int32_t*,
-                          int, int, int, float, int, int, int, int, float*, float*);
+struct SharedArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  int W;
+  const int32_t* ctx;
+  const int32_t* group_starts;
+  const int32_t* group_shared;
+  int num_groups;
+  int nsp;  // shared partitions per group in the grid (0: nothing shared)
+  int hq, hkv, num_blocks;
+  float scale_log2;
+  int part_tokens, max_slots, max_shared_blocks, batch;
+  float* part_out;
+  float* part_lse;
+  float* out;
+  float* lse;
+  const int4* plan;
+  const int* plan_count;
+};
+
+// Launches the shared-prefix pass; returns true when that launch also ran the plan's
+// units (bf16: one matrix-core launch for both), false when the first pass must follow.
+using SharedFn = bool (*)(const SharedArgs&, hipStream_t);
 
 template <typename T, int D, int G>
-void shared_launch(dim3 grid, hipStream_t stream, const void* q, const void* kc, const void* vc,
-                   const int32_t* tables, int W, const int32_t* ctx, const int32_t* gstart,
-                   const int32_t* gshared, int hq, int hkv, int nb, float scale_log2,
-                   int part_tokens, int max_parts, int max_shared_blocks, int batch,
-                   float* part_out, float* part_lse) {
-  hipLaunchKernelGGL((decode_shared_kernel<T, D, G>), grid, dim3(kSharedWaves * kWave), 0,
-                     stream, static_cast<const T*>(q), static_cast<const T*>(kc),
-                     static_cast<const T*>(vc), tables, W, ctx, gstart, gshared, hq, hkv, nb,
-                     scale_log2, part_tokens, max_parts, max_shared_blocks, batch, part_out,
-                     part_lse);
+bool shared_launch(const SharedArgs& a, hipStream_t stream) {
+  const dim3 block(kSharedWaves * kWave);
+  if constexpr (sizeof(T) == 2) {
+    const int groups = a.nsp > 0 ? a.num_groups : 0;
+    const long long wgs = static_cast<long long>(a.nsp) * a.hkv * groups +
+                          static_cast<long long>(a.batch) * a.max_slots * a.hkv;
+    hipLaunchKernelGGL((decode_shared_mfma_kernel<D, G>), dim3(static_cast<unsigned>(wgs)), block,
+                       0, stream, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc),
+                       a.tables, a.W, a.ctx, a.group_starts, a.group_shared, groups,
+                       max(a.nsp, 1), a.hq, a.hkv, a.num_blocks, a.scale_log2, a.part_tokens,
+                       a.max_slots, a.max_shared_blocks, a.batch, a.part_out, a.part_lse, a.out,
+                       a.lse, a.plan, a.plan_count);
+    return true;
+  } else {
+    if (a.nsp > 0)
+      hipLaunchKernelGGL((decode_shared_kernel<T, D, G>), dim3(a.nsp, a.hkv, a.num_groups), block,
+                         0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.kc),
+                         static_cast<const T*>(a.vc), a.tables, a.W, a.ctx, a.group_starts,
+                         a.group_shared, a.hq, a.hkv, a.num_blocks, a.scale_log2, a.part_tokens,
+                         a.max_slots, a.max_shared_blocks, a.batch, a.part_out, a.part_lse);
+    return false;
+  }
 }
 
 template <typename T, int D>
@@ -1132,27 +1546,35 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
     if ((st = launch_status()) != PKV_OK) return st;
   }
   const float scale_log2 = scale_to_log2(scale);
-  if (shared && groups->count > 0 && groups->max_shared_blocks > 0) {
-    const int shared_tokens =
-        min(groups->max_shared_blocks, static_cast<int>(bt_stride)) * kBlockTokens;
-    const int nsp = min(geo.tokens > 0 ? (shared_tokens + geo.tokens - 1) / geo.tokens : 1,
-                        geo.max_slots);
+  bool units_done = false;
+  if (shared) {
+    int nsp = 0;
+    if (groups->count > 0 && groups->max_shared_blocks > 0) {
+      const int shared_tokens =
+          min(groups->max_shared_blocks, static_cast<int>(bt_stride)) * kBlockTokens;
+      nsp = min(geo.tokens > 0 ? (shared_tokens + geo.tokens - 1) / geo.tokens : 1,
+                geo.max_slots);
+    }
     const int G = num_q_heads / num_kv_heads;
     SharedFn sf = dtype == PKV_F32
                       ? (head_dim == 64 ? pick_shared<float, 64>(G) : pick_shared<float, 128>(G))
                       : (head_dim == 64 ? pick_shared<uint16_t, 64>(G)
                                         : pick_shared<uint16_t, 128>(G));
-    sf(dim3(nsp, num_kv_heads, groups->count), s, q, k_cache, v_cache, block_tables,
-       static_cast<int>(bt_stride), context_lens, groups->starts, groups->shared_blocks,
-       num_q_heads, num_kv_heads, num_blocks, scale_log2, geo.tokens, geo.max_slots,
-       groups->max_shared_blocks, batch, w.part_out, w.part_lse);
+    const SharedArgs a{q, k_cache, v_cache, block_tables, static_cast<int>(bt_stride),
+                       context_lens, groups->starts, groups->shared_blocks, groups->count, nsp,
+                       num_q_heads, num_kv_heads, num_blocks, scale_log2, geo.tokens,
+                       geo.max_slots, groups->max_shared_blocks, batch, w.part_out, w.part_lse,
+                       out, lse, w.plan, w.plan_count};
+    units_done = sf(a, s);
     if ((st = launch_status()) != PKV_OK) return st;
   }
-  fn(kOrderPlanned, geo.max_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
-     static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
-     scale_log2, geo.tokens, geo.max_slots, w.part_out, w.part_lse, out, lse, w.plan,
-     w.plan_count);
-  if ((st = launch_status()) != PKV_OK) return st;
+  if (!units_done) {
+    fn(kOrderPlanned, geo.max_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
+       static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
+       scale_log2, geo.tokens, geo.max_slots, w.part_out, w.part_lse, out, lse, w.plan,
+       w.plan_count);
+    if ((st = launch_status()) != PKV_OK) return st;
+  }
   // A separate second pass: merging inside the first pass would need device-scope
   // fences (whole-L2 write-back and invalidate per split workgroup), measured to cost
   // far more than this launch.

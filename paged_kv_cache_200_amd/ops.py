@@ -90,6 +90,12 @@ def decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partit
                                                      max_context_len, partition_size))
 
 
+def shared_prefix_workspace_bytes(batch, num_q_heads, head_dim, max_context_len,
+                                  partition_size) -> int:
+    return int(_lib.lib().pkv_shared_prefix_workspace_bytes(batch, num_q_heads, head_dim,
+                                                            max_context_len, partition_size))
+
+
 def _decode_checks(q, k_cache, v_cache, block_tables, context_lens):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _gpu(t, n)
@@ -236,8 +242,7 @@ def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, 
         lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _gpu(lse, "lse", torch.float32)
-    need = int(_lib.lib().pkv_shared_prefix_workspace_bytes(B, hq, d, int(max_context_len),
-                                                            int(partition_size)))
+    need = shared_prefix_workspace_bytes(B, hq, d, int(max_context_len), int(partition_size))
     workspace, wbytes = _workspace(workspace, need, q.device)
     _lib.call("pkv_paged_decode_shared_prefix", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
               _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),

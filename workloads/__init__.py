@@ -13,9 +13,11 @@ from .synth import (  # noqa: F401
     DecodeCase,
     ReplaySchedule,
     bf16_bits,
+    block_refcounts,
     build_case,
     config_case,
     fork_case,
+    fork_groups,
     parallel_normal,
     replay_schedule,
     replay_step_values,

@@ -291,6 +291,38 @@ def fork_case(name, prefix_lens, forks_per_parent, private_lens, num_q_heads, nu
     return case
 
 
+def fork_groups(case: DecodeCase):
+    """Group layout of a fork case: (group_starts int32 [G + 1], shared_blocks int32 [G]).
+
+    Members of a group are consecutive sequences with the same parent; a group's shared
+    count is the length of the run of leading block ids that all its members' tables hold
+    in common (over the blocks each member uses)."""
+    if case.fork_parent is None:
+        raise ValueError("not a fork case")
+    parent = case.fork_parent.tolist()
+    starts = [0] + [s for s in range(1, len(parent)) if parent[s] != parent[s - 1]]
+    starts.append(len(parent))
+    shared = []
+    for g in range(len(starts) - 1):
+        rows = range(starts[g], starts[g + 1])
+        used = min(-(-int(case.context_lens[s]) // BLOCK_SIZE) for s in rows)
+        k = 0
+        while k < used and len({int(case.block_tables[s, k]) for s in rows}) == 1:
+            k += 1
+        shared.append(k)
+    return np.asarray(starts, np.int32), np.asarray(shared, np.int32)
+
+
+def block_refcounts(case: DecodeCase) -> dict:
+    """Physical block id -> number of sequences whose used blocks include it."""
+    refs = {}
+    for s, n in enumerate(case.context_lens.tolist()):
+        for j in range(-(-n // BLOCK_SIZE)):
+            b = int(case.block_tables[s, j])
+            refs[b] = refs.get(b, 0) + 1
+    return refs
+
+
 # --------------------------------------------------------------------------------------
 # The five workload shapes.  Distribution parameters the pages leave open are fixed
 # here (lognormal sigma = ln 2 so that the stated maximum is 8x the median, i.e. e^(3 sigma)).
