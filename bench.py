@@ -44,8 +44,9 @@ def parse_args():
                    choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny",
                             "gpt2_replay"])
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--partition-size", type=int, default=4096,
-                   help="KV partition size (the long-context workload fixes 512, tiny uses 0)")
+    p.add_argument("--partition-size", type=int, default=None,
+                   help="split-KV partition size in tokens (default: the workload's own, else "
+                        "1024 for fork groups on the shared-prefix path, else 4096)")
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -263,7 +264,11 @@ def main():
 
     print(f"[bench] building inputs: {args.workload} seed {args.seed}", file=sys.stderr, flush=True)
     case = config_case(args.workload, args.seed)
-    P = case.extra.get("partition_size", args.partition_size)
+    shared_path = case.fork_parent is not None and not args.no_shared_prefix
+    if args.partition_size is not None:
+        P = args.partition_size
+    else:
+        P = case.extra.get("partition_size", 1024 if shared_path else 4096)
     if args.workload == "tiny":
         P = 0
     B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
@@ -304,7 +309,6 @@ def main():
     k_new, v_new = to_dev(kn), to_dev(vn)
     out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
-    shared_path = case.fork_parent is not None and not args.no_shared_prefix
     if shared_path:
         gs_np, gb_np = fork_groups(case)
         gstarts, gblocks, max_shared = to_dev(gs_np), to_dev(gb_np), int(gb_np.max())

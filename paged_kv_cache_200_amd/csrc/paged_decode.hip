@@ -897,30 +897,31 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(
 // Matrix-core version (bf16 cache).  The group's query rows, (member, query head) pairs,
 // 16 per tile, are attended together against each shared block, which is read once per
 // tile through the first member's table row: 16 x 16 score tiles S^T = K Q^T on the bf16
-// MFMA (16x16x32), then O += P V on the fp32 MFMA (16x16x4), so the probabilities enter
-// the product unrounded.  Four waves take the range's blocks round-robin, each with its
+// MFMA (16x16x32), then O += P V on the bf16 MFMA (16x16x16) with P carried as a sum
+// of two bf16 terms.  Four waves take the range's blocks round-robin, each with its
 // own online softmax per row, and are merged through LDS.  A member whose table row does
 // not hold the same block ids over its share of the range is attended separately through
 // its own row, so the result never depends on the sharing being real.
 //
 // Lane layouts (c = lane % 16, h = lane / 16):
-//   S^T tile: lane holds rows c, tokens 4h + r (r = 0..3) of the block.  The score
-//     contraction runs over dims permuted so that lane h-group loads one contiguous D/4
-//     run: K[token c][h * D/4 + 8k ..] and Q[row c][h * D/4 + 8k ..].
-//   P V step k (k = 0..3): A = P[row c][token 4h + k] (the lane's own score r = k),
-//     B = V[token 4h + k][c * D/16 + j] for output tile j, so lane loads the D/16
-//     contiguous dims c * D/16 .. of 4 tokens.
+//   S^T tile: lane holds rows c, tokens 4h + r (r = 0..3) of the block.  Score step k
+//     contracts dims 32k .. 32k + 31, lane h-group taking 8 of them: K[token c][32k + 8h ..]
+//     and Q[row c][32k + 8h ..], so one load instruction reads 64 contiguous bytes of
+//     every token row.
+//   P V, output tile j: A = P[row c][tokens 4h .. 4h + 3] (the lane's own scores),
+//     B = V[tokens 4h .. 4h + 3][c * D/16 + j], so lane loads the D/16 contiguous dims
+//     c * D/16 .. of 4 tokens.
 //   O tile j: lane holds rows 4h + r, dim c * D/16 + j.
 constexpr int kMfmaRows = 16;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct MfmaGeom {
   static constexpr int kQkSteps = D / 32;   // 16x16x32 steps over the head dim
-  static constexpr int kRun = D / 4;        // contiguous dims per lane in the score step
   static constexpr int kTiles = D / 16;     // output tiles of 16 dims
   static constexpr int kVWords = D / 32;    // 32-bit words of V per lane and token
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
@@ -938,7 +939,7 @@ __device__ __forceinline__ void mfma_load_block(MfmaBlock<D>& b, const uint16_t*
   using Mg = MfmaGeom<D>;
 #pragma unroll
   for (int k = 0; k < Mg::kQkSteps; ++k)
-    b.k[k] = *reinterpret_cast<const u32x4_t*>(kt + c * D + h * Mg::kRun + 8 * k);
+    b.k[k] = *reinterpret_cast<const u32x4_t*>(kt + c * D + 32 * k + 8 * h);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint16_t* src = vt + (4 * h + k) * D + c * Mg::kTiles;
@@ -954,28 +955,32 @@ __device__ __forceinline__ void mfma_load_block(MfmaBlock<D>& b, const uint16_t*
   }
 }
 
-// LDS of one row tile: per member its token limit and whether its table row matches the
-// tile leader's; per wave and row the softmax state and the unnormalised output.
+// LDS of one row tile: per wave the members found not to share the leader's blocks, and
+// per wave and row the softmax state and the unnormalised output.
 template <int D>
 struct MfmaShared {
-  int n[kMfmaRows];
-  int mismatch[kMfmaRows];
+  unsigned mismatch[kSharedWaves];
   float m[kSharedWaves][kMfmaRows];
   float l[kSharedWaves][kMfmaRows];
   float4 o[kSharedWaves][kMfmaRows][D / 4];
 };
 
-// Rows of the members selected by `take` (bit mi: member base + mi), attended over
-// tokens [tok0, sm.n[mi]) through table row `lead`; row (s, h) is written to
-// dst_out[(s * Hq + h) * slots + slot] (D floats) and dst_lse[...] (nullable).  Called by
-// all threads of the workgroup (it synchronises).
+// Attends the rows of the members selected by `take` (bit mi: sequence base + mi) over
+// tokens [tok0, min(n_mi, tok1)) through table row `lead_seq`, and writes row (s, h) to
+// dst_out[(s * Hq + h) * slots + slot] (D floats) and dst_lse[...] (nullable).
+//
+// check: also compare every selected member's block ids with the leader's over the
+// member's share of the range (in the same loads that fetch the leader's ids).  Members
+// that differ come back as the result; if there are any, nothing is written and the
+// caller redoes the others without them and each of them through its own row.  Called
+// by all threads of the workgroup (it synchronises).
 template <int D, int G>
-__device__ __forceinline__ void mfma_tile(
+__device__ __forceinline__ unsigned mfma_tile(
     MfmaShared<D>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ lead, int base,
-    unsigned take, int kvh, int num_q_heads, int num_kv_heads, int num_blocks,
-    float scale_log2, int tok0, int slot, int slots, float* __restrict__ dst_out,
-    float* __restrict__ dst_lse) {
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
+    const int32_t* __restrict__ ctx_lens, int lead_seq, int base, unsigned take, bool check,
+    int kvh, int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int tok0,
+    int tok1, int slot, int slots, float* __restrict__ dst_out, float* __restrict__ dst_lse) {
   using Mg = MfmaGeom<D>;
   constexpr int kMembers = kMfmaRows / G;
   constexpr int kRows = kMembers * G;
@@ -987,23 +992,34 @@ __device__ __forceinline__ void mfma_tile(
   const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
   const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
   const int b0 = tok0 / kBlockTokens;
+  const int cap = W * kBlockTokens;
+  const int32_t* lead = tables + static_cast<size_t>(lead_seq) * W;
 
+  // Token limit of each selected member (uniform), the largest, and this lane's row's.
+  int nmem[kMembers];
   int n_max = 0;
+  int n_c = 0;
 #pragma unroll
-  for (int mi = 0; mi < kMembers; ++mi)
-    if ((take >> mi) & 1u) n_max = max(n_max, sm.n[mi]);
-  const bool c_live = c < kRows && ((take >> (c / G)) & 1u);
-  const int n_c = c_live ? sm.n[c / G] : 0;
+  for (int mi = 0; mi < kMembers; ++mi) {
+    int n = 0;
+    if ((take >> mi) & 1u) {
+      n = ctx_lens[base + mi];
+      n = n < 0 ? 0 : min(min(n, cap), tok1);
+    }
+    nmem[mi] = n;
+    n_max = max(n_max, n);
+    if (c < kRows && c / G == mi) n_c = n;
+  }
 
   // Query rows as the B operand of the score step (zero for rows not taken).
   u32x4_t qr[Mg::kQkSteps];
 #pragma unroll
   for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = u32x4_t{0u, 0u, 0u, 0u};
-  if (c_live) {
+  if (c < kRows && ((take >> (c / G)) & 1u)) {
     const uint16_t* qrow =
-        q + (static_cast<size_t>(base + c / G) * num_q_heads + kvh * G + c % G) * D + h * Mg::kRun;
+        q + (static_cast<size_t>(base + c / G) * num_q_heads + kvh * G + c % G) * D + 8 * h;
 #pragma unroll
-    for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * k);
+    for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
   }
 
   float m_c = -INFINITY;  // running max of row c, log2 units (lazy, as in the first pass)
@@ -1014,17 +1030,24 @@ __device__ __forceinline__ void mfma_tile(
 
   const int nblk = n_max > tok0 ? (n_max - tok0 + kBlockTokens - 1) / kBlockTokens : 0;
   const int nw = nblk > wave ? (nblk - wave + kSharedWaves - 1) / kSharedWaves : 0;
+  unsigned mism = 0;  // members whose ids differ on this wave's blocks
   // Block ids of this wave's blocks, 64 at a time, one per lane.
   int id_base = 0;
   auto fetch_ids = [&](int from) -> int {
     const int k = from + lane;
-    int id = 0;
-    bool bad = false;
-    if (k < nw) {
-      id = lead[b0 + wave + kSharedWaves * k];
-      bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
-      id = bad ? 0 : id;
+    const bool live = k < nw;
+    const int b = b0 + wave + kSharedWaves * k;
+    int id = live ? lead[b] : 0;
+    if (check) {
+#pragma unroll
+      for (int mi = 0; mi < kMembers; ++mi) {
+        const bool differs = live && b * kBlockTokens < nmem[mi] &&
+                             tables[static_cast<size_t>(base + mi) * W + b] != id;
+        if (__any(differs)) mism |= 1u << mi;
+      }
     }
+    const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
+    id = bad ? 0 : id;
     if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
     return id;
   };
@@ -1038,7 +1061,7 @@ __device__ __forceinline__ void mfma_tile(
     const size_t off = static_cast<size_t>(id) * block_elems + kvh * head_elems;
     mfma_load_block<D>(bl, kc + off, vc + off, c, h);
   };
-  auto process = [&](const MfmaBlock<D>& cur, int k) {
+  auto process = [&](MfmaBlock<D>& cur, int k) {
     const int t_base = (b0 + wave + kSharedWaves * k) * kBlockTokens;  // token of slot 0
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -1079,18 +1102,43 @@ __device__ __forceinline__ void mfma_tile(
       p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - m_c);
       l_part += p[i];
     }
-    // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
-    const bool tail = t_base + kBlockTokens > n_max;
+    // P V on the bf16 MFMA with P split into two bf16 terms, hi = P truncated and
+    // lo = (P - hi) truncated (P - hi is exact in fp32), so the product sees P to about
+    // 2^-16 relative.  A operand: P[row c][tokens 4h .. 4h + 3], the lane's own scores.
+    uint32_t hb[4], lb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool vok = !tail || (t_base + 4 * h + i < n_max);
+      hb[i] = __float_as_uint(p[i]) & 0xffff0000u;
+      lb[i] = __float_as_uint(p[i] - __uint_as_float(hb[i])) & 0xffff0000u;
+    }
+    const i16x4_t a_hi = __builtin_bit_cast(
+        i16x4_t, u32x2_t{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3]});
+    const i16x4_t a_lo = __builtin_bit_cast(
+        i16x4_t, u32x2_t{(lb[0] >> 16) | lb[1], (lb[2] >> 16) | lb[3]});
+    // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
+    if (t_base + kBlockTokens > n_max) {
 #pragma unroll
-      for (int w = 0; w < Mg::kVWords; ++w) {
-        const uint32_t bits = vok ? cur.v[i][w] : 0u;
-        o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], bf16_lo(bits), o[2 * w], 0, 0, 0);
-        o[2 * w + 1] =
-            __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], bf16_hi(bits), o[2 * w + 1], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const bool vok = t_base + 4 * h + i < n_max;
+#pragma unroll
+        for (int w = 0; w < Mg::kVWords; ++w) cur.v[i][w] = vok ? cur.v[i][w] : 0u;
       }
+    }
+    const auto& v = cur.v;
+    // B operand of tile j: V[tokens 4h .. 4h + 3][dim c * D/16 + j], the even tiles from
+    // the low halves of the lane's words, the odd ones from the high halves.
+#pragma unroll
+    for (int w = 0; w < Mg::kVWords; ++w) {
+      const i16x4_t b_even = __builtin_bit_cast(
+          i16x4_t, u32x2_t{(v[0][w] & 0xffffu) | (v[1][w] << 16),
+                           (v[2][w] & 0xffffu) | (v[3][w] << 16)});
+      const i16x4_t b_odd = __builtin_bit_cast(
+          i16x4_t, u32x2_t{(v[0][w] >> 16) | (v[1][w] & 0xffff0000u),
+                           (v[2][w] >> 16) | (v[3][w] & 0xffff0000u)});
+      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_even, o[2 * w], 0, 0, 0);
+      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_even, o[2 * w], 0, 0, 0);
+      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_odd, o[2 * w + 1], 0, 0, 0);
+      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_odd, o[2 * w + 1], 0, 0, 0);
     }
   };
   // Two blocks in flight: the next block's loads are issued before this one's math.
@@ -1114,6 +1162,7 @@ __device__ __forceinline__ void mfma_tile(
     sm.m[wave][c] = m_c;
     sm.l[wave][c] = l_c;
   }
+  if (lane == 0) sm.mismatch[wave] = mism;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -1122,10 +1171,18 @@ __device__ __forceinline__ void mfma_tile(
           make_float4(o[4 * u][i], o[4 * u + 1][i], o[4 * u + 2][i], o[4 * u + 3][i]);
   }
   __syncthreads();
+  unsigned differ = 0;
+#pragma unroll
+  for (int w = 0; w < kSharedWaves; ++w) differ |= sm.mismatch[w];
+  differ &= take;
+  // A member that does not share streamed the leader's blocks up to its own length,
+  // which can include slots stale for everyone (NaN V times a zero weight spoils every
+  // row), so a tile with any such member writes nothing and is redone without it.
+  const unsigned write = differ != 0 ? 0u : take;
   const int row = tid / 16;  // 16 rows x 16 threads of D/16 dims
   const int cc = tid % 16;
   const int mi = row / G;
-  if (row < kRows && ((take >> mi) & 1u)) {
+  if (row < kRows && ((write >> mi) & 1u)) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kSharedWaves; ++w) M = fmaxf(M, sm.m[w][row]);
@@ -1158,6 +1215,7 @@ __device__ __forceinline__ void mfma_tile(
       dst_lse[sh * slots + slot] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();  // LDS reused by the next call
+  return differ;
 }
 
 // One launch for a batch of fork groups: workgroups [0, shared_wgs) are (shared partition,
@@ -1178,8 +1236,6 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kerne
     const int4* __restrict__ plan, const int* __restrict__ plan_count) {
   constexpr int kMembers = kMfmaRows / G;  // members per row tile
   __shared__ MfmaShared<D> sm;
-  const int tid = threadIdx.x;
-  const int cap = W * kBlockTokens;
   const int shared_wgs = nsp_grid * num_kv_heads * num_groups;
   const int x = blockIdx.x;
   if (x >= shared_wgs) {
@@ -1187,17 +1243,9 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kerne
     const int kvh = (x - shared_wgs) % num_kv_heads;
     if (u >= *plan_count) return;
     const int4 e = plan[u];
-    const int s = e.x;
-    const int slot = e.w & kSlotMask;
     const bool direct = (e.w & kDirectFlag) != 0;
-    if (tid == 0) {
-      int n = ctx_lens[s];
-      n = n < 0 ? 0 : min(n, cap);
-      sm.n[0] = min(n, e.z);
-    }
-    __syncthreads();
-    mfma_tile<D, G>(sm, q, kc, vc, tables + static_cast<size_t>(s) * W, s, 1u, kvh, num_q_heads,
-                    num_kv_heads, num_blocks, scale_log2, e.y, direct ? 0 : slot,
+    mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, e.x, e.x, 1u, false, kvh, num_q_heads,
+                    num_kv_heads, num_blocks, scale_log2, e.y, e.z, direct ? 0 : e.w & kSlotMask,
                     direct ? 1 : max_parts, direct ? out : part_out, direct ? lse : part_lse);
     return;
   }
@@ -1206,42 +1254,24 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kerne
   const SharedRange r = shared_range(group_starts, group_shared_blocks, x / (nsp_grid * num_kv_heads),
                                      part, part_tokens, max_parts, max_shared_blocks, W, batch);
   if (!r.live) return;
-  const int b0 = r.tok0 / kBlockTokens;
-  const int span = (r.tok1 - r.tok0 + kBlockTokens - 1) / kBlockTokens;
   for (int base = r.m0; base < r.m1; base += kMembers) {
     const int cnt = min(kMembers, r.m1 - base);
-    if (tid < kMembers) {
-      int n = tid < cnt ? ctx_lens[base + tid] : 0;
-      n = n < 0 ? 0 : min(n, cap);
-      sm.n[tid] = min(n, r.tok1);
-      sm.mismatch[tid] = 0;
-    }
-    __syncthreads();
-    // Compare each member's block ids over its share of the range with the tile leader's.
-    const int32_t* lead = tables + static_cast<size_t>(base) * W;
-    for (int i = tid; i < cnt * span; i += kSharedWaves * kWave) {
-      const int mi = i / span;
-      const int b = b0 + i % span;
-      if (b * kBlockTokens < sm.n[mi] && tables[static_cast<size_t>(base + mi) * W + b] != lead[b])
-        sm.mismatch[mi] = 1;
-    }
-    __syncthreads();
-    unsigned shared_take = 0;
-    for (int mi = 0; mi < cnt; ++mi) shared_take |= sm.mismatch[mi] ? 0u : (1u << mi);
-    // Pass 0: the members that share, through the leader's row.  Then one pass per member
-    // whose ids differ (the sharing hint was wrong), through its own row.
-    unsigned pending = ~shared_take & ((1u << cnt) - 1u);
-    for (int pass = 0; pass == 0 || pending != 0; ++pass) {
-      unsigned take = shared_take;
-      const int32_t* row = lead;
-      if (pass > 0) {
-        const int mi = __builtin_ctz(pending);
-        pending &= pending - 1u;
-        take = 1u << mi;
-        row = tables + static_cast<size_t>(base + mi) * W;
-      }
-      mfma_tile<D, G>(sm, q, kc, vc, row, base, take, kvh, num_q_heads, num_kv_heads,
-                      num_blocks, scale_log2, r.tok0, part, max_parts, part_out, part_lse);
+    // The tile's members through the first one's row; if the sharing hint was wrong for
+    // some, the others again without them, then each of them through its own row.
+    const unsigned all = (1u << cnt) - 1u;
+    unsigned differ = mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, base, base, all, true,
+                                      kvh, num_q_heads, num_kv_heads, num_blocks, scale_log2,
+                                      r.tok0, r.tok1, part, max_parts, part_out, part_lse);
+    if (differ != 0 && (all & ~differ) != 0)
+      mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, base, base, all & ~differ, false, kvh,
+                      num_q_heads, num_kv_heads, num_blocks, scale_log2, r.tok0, r.tok1, part,
+                      max_parts, part_out, part_lse);
+    while (differ != 0) {
+      const int mi = __builtin_ctz(differ);
+      differ &= differ - 1u;
+      mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, base + mi, base, 1u << mi, false, kvh,
+                      num_q_heads, num_kv_heads, num_blocks, scale_log2, r.tok0, r.tok1, part,
+                      max_parts, part_out, part_lse);
     }
   }
 }

@@ -88,3 +88,30 @@ def test_malformed_groups_flag_an_error():
         flags = ops.device_error()
         assert flags & 32, (starts, flags)
     assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_copied_member_with_stale_hint(P):
+    """One member of a real fork group had its prefix blocks copied (same contents, new
+    ids) while the hint still counts them as shared; a sibling is shorter than the prefix.
+    Outputs must equal the plain decode."""
+    say(f"copied member, stale hint, P={P}")
+    case = fork_case("copied", [96, 160], [4, 3], [[0, 16, 40, 3], [7, 0, 33]], 32, 8, 128,
+                     "bf16", seed=21, pool_factor=3.0)
+    refs = {}
+    for s, n in enumerate(case.context_lens.tolist()):
+        for j in range(-(-n // 16)):
+            refs.setdefault(int(case.block_tables[s, j]), []).append(s)
+    free = [b for b in range(case.num_blocks) if b not in refs and b != case.poison_block]
+    victim = 2  # third member of the first group
+    for j in range(96 // 16):
+        src, dst = int(case.block_tables[victim, j]), free.pop()
+        case.k_pool[:, dst] = case.k_pool[:, src]
+        case.v_pool[:, dst] = case.v_pool[:, src]
+        case.block_tables[victim, j] = dst
+    case.context_lens[1] = 40  # shorter than the 96-token prefix: stops inside it
+    starts = [0, 4, 7]
+    dc = DeviceCase(case)
+    assert_parity(_shared_decode(dc, starts, [6, 10], P), oracle_decode(case), "bf16",
+                  f"copied member P{P}")
+    assert_no_device_error()
