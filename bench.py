@@ -326,10 +326,12 @@ def main():
     def step():
         for l in range(layers):
             if shared_path:
-                # fork groups: append, then one decode call that streams each group's
-                # shared blocks once for all members
-                pkv.kv_append(kcs[l], vcs[l], k_new, v_new, tables, start, cu)
-                shared_decode(l)
+                # fork groups: append and work plan in one launch, then one decode launch
+                # that streams each group's shared blocks once for all members
+                pkv.append_paged_decode_shared_prefix(
+                    qs[l], kcs[l], vcs[l], k_new, v_new, tables, start, cu, ctx, gstarts,
+                    gblocks, max_shared, max_ctx, scale=scale, partition_size=P, out=out,
+                    lse=lse, workspace=ws)
             else:
                 # kv_append + paged_decode in one library call (append and work plan
                 # share a launch)
@@ -456,7 +458,8 @@ def main():
             "num_blocks": case.num_blocks,
             "layers": layers,
             "partition_size": P,
-            "step": ("append + shared-prefix decode (plan, shared pass, first pass, combine)"
+            "step": ("append + work plan (one launch), shared-prefix and private ranges (one "
+                     "launch), LSE combine"
                      if shared_path else
                      "append 1 token/seq + work plan (one launch), split-KV first pass, "
                      "LSE combine"),

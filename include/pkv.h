@@ -199,8 +199,9 @@ int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache
  * Decode for a batch holding copy-on-write fork groups (spindle, "Paging":
  * forked sequences share blocks through reference counts).  Computes the
  * same out and lse as pkv_paged_decode (equal within rounding; the shared
- * prefix adds a partition boundary, so not bit for bit), but each group's
- * shared leading blocks are streamed by one workgroup for all its members.
+ * prefix adds a partition boundary and, for bf16 caches, the scores and the
+ * weighted sum run on matrix cores, so not bit for bit), but each group's
+ * shared leading blocks are streamed once for all its members.
  *
  *   group_starts        : int32 [num_groups + 1]: group g is sequences
  *                         [group_starts[g], group_starts[g + 1]); the groups
@@ -209,15 +210,19 @@ int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache
  *                         shares nothing is a group of one.
  *   group_shared_blocks : int32 [num_groups]: leading logical blocks that
  *                         every member of g holds in common (same block ids).
- *                         A hint for efficiency only: every member is read
- *                         through its own table, so results never depend on
- *                         it.  Values above max_shared_blocks (host) are
- *                         clamped; the rest is attended as private context.
+ *                         A hint for efficiency only: a member whose ids
+ *                         differ is detected and attended through its own
+ *                         table row, so results never depend on it.  Values
+ *                         above max_shared_blocks (host) are clamped; the
+ *                         rest is attended as private context.
  * Each member's tokens [shared, context_lens[s]) are split into partitions
  * of partition_size (0: one) after the shared prefix's own partitions.
  * workspace: pkv_shared_prefix_workspace_bytes(...) bytes, 256-byte aligned.
- * Malformed groups set PKV_DEVERR_GROUPS (results then unspecified).
- * Launches: plan, shared-prefix pass, first pass, combine.
+ * Malformed groups set PKV_DEVERR_GROUPS (results then unspecified; every
+ * access stays in bounds).
+ * Launches: plan; then for bf16 one kernel for the shared prefixes and the
+ * private ranges (fp32: the shared-prefix pass, then the first pass); then
+ * the combine.
  */
 size_t pkv_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);
@@ -233,6 +238,23 @@ int pkv_paged_decode_shared_prefix(float* out, float* lse, const void* q, const 
                                    int32_t max_context_len, float scale, int32_t partition_size,
                                    void* workspace, size_t workspace_bytes, int32_t dtype,
                                    pkv_stream_t stream);
+
+/*
+ * pkv_kv_append followed by pkv_paged_decode_shared_prefix, with the append
+ * and the work plan in one launch (as pkv_append_paged_decode does for the
+ * plain decode).  The appended tokens must not land in a block that several
+ * sequences hold (copy-on-write: the caller copies such a block first, see
+ * pkv_copy_blocks).  Arguments as in those two calls.
+ */
+int pkv_append_paged_decode_shared_prefix(
+    float* out, float* lse, const void* q, void* k_cache, void* v_cache, const void* k_new,
+    const void* v_new, const int32_t* block_tables, int64_t bt_stride, const int32_t* start_pos,
+    const int32_t* cu_new_tokens, int32_t total_new, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* group_shared_blocks, int32_t num_groups,
+    int32_t max_shared_blocks, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+    pkv_stream_t stream);
 
 /*
  * First pass only: per-partition attention, no merge.

@@ -10,6 +10,7 @@ using the ops without it raises.
 from .ops import (  # noqa: F401
     BLOCK_SIZE,
     append_paged_decode,
+    append_paged_decode_shared_prefix,
     copy_blocks,
     decode_plan,
     decode_workspace_bytes,

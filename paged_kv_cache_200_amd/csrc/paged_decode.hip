@@ -1691,6 +1691,35 @@ extern "C" int pkv_paged_decode_planned(float* out, float* lse, const void* q,
                      workspace_bytes, dtype, stream);
 }
 
+namespace {
+// Validates and packs the append arguments of the append-and-decode entry points.
+int make_append(const void* k_new, const void* v_new, const int32_t* start_pos,
+                const int32_t* cu_new_tokens, int32_t total_new, AppendArgs* a) {
+  if (total_new < 0) return PKV_ERR_SHAPE;
+  if (total_new > 0) {
+    if (!k_new || !v_new || !start_pos || !cu_new_tokens) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ARG;
+    a->k_new = k_new;
+    a->v_new = v_new;
+    a->start_pos = start_pos;
+    a->cu = cu_new_tokens;
+    a->total = total_new;
+  }
+  return PKV_OK;
+}
+
+int make_groups(const int32_t* group_starts, const int32_t* group_shared_blocks,
+                int32_t num_groups, int32_t max_shared_blocks, int32_t batch, Groups* g) {
+  if (num_groups < 0 || max_shared_blocks < 0 || num_groups > batch) return PKV_ERR_SHAPE;
+  if (batch > 0 && (!group_starts || !group_shared_blocks)) return PKV_ERR_NULL;
+  g->starts = group_starts;
+  g->shared_blocks = group_shared_blocks;
+  g->count = num_groups;
+  g->max_shared_blocks = max_shared_blocks;
+  return PKV_OK;
+}
+}  // namespace
+
 extern "C" int pkv_append_paged_decode(
     float* out, float* lse, const void* q, void* k_cache, void* v_cache, const void* k_new,
     const void* v_new, const int32_t* block_tables, int64_t bt_stride, const int32_t* start_pos,
@@ -1698,17 +1727,9 @@ extern "C" int pkv_append_paged_decode(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
     void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
-  if (total_new < 0) return PKV_ERR_SHAPE;
   AppendArgs a;
-  if (total_new > 0) {
-    if (!k_new || !v_new || !start_pos || !cu_new_tokens) return PKV_ERR_NULL;
-    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ARG;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.start_pos = start_pos;
-    a.cu = cu_new_tokens;
-    a.total = total_new;
-  }
+  const int st = make_append(k_new, v_new, start_pos, cu_new_tokens, total_new, &a);
+  if (st != PKV_OK) return st;
   return decode_impl(true, out, lse, q, k_cache, v_cache, block_tables, bt_stride, context_lens,
                      batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
@@ -1723,17 +1744,35 @@ extern "C" int pkv_paged_decode_shared_prefix(
     int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
     float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
     pkv_stream_t stream) {
-  if (num_groups < 0 || max_shared_blocks < 0 || num_groups > batch) return PKV_ERR_SHAPE;
-  if (batch > 0 && (!group_starts || !group_shared_blocks)) return PKV_ERR_NULL;
   Groups g;
-  g.starts = group_starts;
-  g.shared_blocks = group_shared_blocks;
-  g.count = num_groups;
-  g.max_shared_blocks = max_shared_blocks;
+  const int st =
+      make_groups(group_starts, group_shared_blocks, num_groups, max_shared_blocks, batch, &g);
+  if (st != PKV_OK) return st;
   return decode_impl(true, out, lse, q, k_cache, v_cache, block_tables, bt_stride, context_lens,
                      batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
                      stream, nullptr, &g);
+}
+
+extern "C" int pkv_append_paged_decode_shared_prefix(
+    float* out, float* lse, const void* q, void* k_cache, void* v_cache, const void* k_new,
+    const void* v_new, const int32_t* block_tables, int64_t bt_stride, const int32_t* start_pos,
+    const int32_t* cu_new_tokens, int32_t total_new, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* group_shared_blocks, int32_t num_groups,
+    int32_t max_shared_blocks, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+    pkv_stream_t stream) {
+  AppendArgs a;
+  Groups g;
+  int st = make_append(k_new, v_new, start_pos, cu_new_tokens, total_new, &a);
+  if (st != PKV_OK) return st;
+  st = make_groups(group_starts, group_shared_blocks, num_groups, max_shared_blocks, batch, &g);
+  if (st != PKV_OK) return st;
+  return decode_impl(true, out, lse, q, k_cache, v_cache, block_tables, bt_stride, context_lens,
+                     batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                     stream, &a, &g);
 }
 
 extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,

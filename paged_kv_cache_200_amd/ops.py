@@ -183,15 +183,7 @@ def paged_decode_planned(q, k_cache, v_cache, block_tables, context_lens, max_co
                    max_context_len, scale, partition_size, out, lse, workspace, want_lse, stream)
 
 
-def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
-                        cu_new_tokens, context_lens, max_context_len, scale=None,
-                        partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
-                        stream=None):
-    """kv_append then paged_decode in one call (append and work plan share a launch).
-
-    context_lens must already count the appended tokens.
-    """
-    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+def _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d):
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _gpu(t, n)
         _same_kind(k_cache, t, n)
@@ -201,15 +193,41 @@ def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_p
     _gpu(cu_new_tokens, "cu_new_tokens", torch.int32)
     if start_pos.shape != (B,) or cu_new_tokens.shape != (B + 1,):
         raise ValueError("start_pos [B] and cu_new_tokens [B + 1] expected")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
+
+
+def _group_checks(group_starts, group_shared_blocks):
+    _gpu(group_starts, "group_starts", torch.int32)
+    _gpu(group_shared_blocks, "group_shared_blocks", torch.int32)
+    G = group_shared_blocks.shape[0]
+    if group_starts.shape != (G + 1,):
+        raise ValueError("group_starts must have num_groups + 1 entries")
+    return G
+
+
+def _outputs(out, lse, want_lse, B, hq, d, device):
     if out is None:
-        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=device)
     _gpu(out, "out", torch.float32)
     if lse is None and want_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, hq), dtype=torch.float32, device=device)
     if lse is not None:
         _gpu(lse, "lse", torch.float32)
+    return out, lse
+
+
+def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
+                        cu_new_tokens, context_lens, max_context_len, scale=None,
+                        partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
+                        stream=None):
+    """kv_append then paged_decode in one call (append and work plan share a launch).
+
+    context_lens must already count the appended tokens.
+    """
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
     need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
     workspace, wbytes = _workspace(workspace, need, q.device)
     _lib.call("pkv_append_paged_decode", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
@@ -228,20 +246,10 @@ def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, 
     """Decode a batch of copy-on-write fork groups, streaming each group's shared
     leading blocks once for all members (see pkv_paged_decode_shared_prefix)."""
     B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
-    _gpu(group_starts, "group_starts", torch.int32)
-    _gpu(group_shared_blocks, "group_shared_blocks", torch.int32)
-    G = group_shared_blocks.shape[0]
-    if group_starts.shape != (G + 1,):
-        raise ValueError("group_starts must have num_groups + 1 entries")
+    G = _group_checks(group_starts, group_shared_blocks)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
-    _gpu(out, "out", torch.float32)
-    if lse is None and want_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _gpu(lse, "lse", torch.float32)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
     need = shared_prefix_workspace_bytes(B, hq, d, int(max_context_len), int(partition_size))
     workspace, wbytes = _workspace(workspace, need, q.device)
     _lib.call("pkv_paged_decode_shared_prefix", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
@@ -249,6 +257,31 @@ def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, 
               _ptr(group_starts), _ptr(group_shared_blocks), G, int(max_shared_blocks), B, hq,
               hkv, d, BLOCK_SIZE, nb, int(max_context_len), float(scale), int(partition_size),
               _ptr(workspace), wbytes, _kv_code(k_cache), _stream(stream))
+    return out, lse
+
+
+def append_paged_decode_shared_prefix(q, k_cache, v_cache, k_new, v_new, block_tables,
+                                      start_pos, cu_new_tokens, context_lens, group_starts,
+                                      group_shared_blocks, max_shared_blocks, max_context_len,
+                                      scale=None, partition_size=0, out=None, lse=None,
+                                      workspace=None, want_lse=True, stream=None):
+    """kv_append then paged_decode_shared_prefix, append and work plan in one launch.
+    New tokens must not land in a block that several sequences hold."""
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
+    G = _group_checks(group_starts, group_shared_blocks)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+    need = shared_prefix_workspace_bytes(B, hq, d, int(max_context_len), int(partition_size))
+    workspace, wbytes = _workspace(workspace, need, q.device)
+    _lib.call("pkv_append_paged_decode_shared_prefix", _ptr(out), _ptr(lse), _ptr(q),
+              _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+              block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
+              _ptr(context_lens), _ptr(group_starts), _ptr(group_shared_blocks), G,
+              int(max_shared_blocks), B, hq, hkv, d, BLOCK_SIZE, nb, int(max_context_len),
+              float(scale), int(partition_size), _ptr(workspace), wbytes, _kv_code(k_cache),
+              _stream(stream))
     return out, lse
 
 

@@ -115,3 +115,49 @@ def test_copied_member_with_stale_hint(P):
     assert_parity(_shared_decode(dc, starts, [6, 10], P), oracle_decode(case), "bf16",
                   f"copied member P{P}")
     assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_append_and_shared_decode_in_one_call(P):
+    """append_paged_decode_shared_prefix == kv_append, then paged_decode_shared_prefix
+    (bit for bit), and the appended cache equals the oracle's append."""
+    from oracle import paged_attention as pa
+    from paged_kv_cache_200_amd import ops
+    say(f"append + shared decode in one call, P={P}")
+    prefixes, forks = [64, 128], [3, 2]
+    privates = [[5, 16, 30], [1, 47]]
+    case = fork_case("append", prefixes, forks, privates, 32, 8, 128, "bf16", seed=4)
+    B, hkv, d = case.batch, case.num_kv_heads, case.head_dim
+    rng = np.random.default_rng(9)
+    # one new token per member, at its last position (inside its private blocks)
+    start = (case.context_lens - 1).astype(np.int32)
+    cu = np.arange(B + 1, dtype=np.int32)
+    kn = (rng.standard_normal((B, hkv, d), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vn = (rng.standard_normal((B, hkv, d), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    starts = np.array([0, 3, 5], np.int32)
+    shared = np.array([4, 8], np.int32)
+    results = []
+    for fused in (True, False):
+        dc = DeviceCase(case)
+        args = (dev(kn), dev(vn), dc.tables, dev(start), dev(cu))
+        if fused:
+            o, l = ops.append_paged_decode_shared_prefix(
+                dc.q, dc.k, dc.v, *args, dc.ctx, dev(starts), dev(shared), 8, dc.max_ctx,
+                scale=float(case.scale), partition_size=P)
+        else:
+            ops.kv_append(dc.k, dc.v, *args)
+            o, l = ops.paged_decode_shared_prefix(dc.q, dc.k, dc.v, dc.tables, dc.ctx,
+                                                  dev(starts), dev(shared), 8, dc.max_ctx,
+                                                  scale=float(case.scale), partition_size=P)
+        torch.cuda.synchronize()
+        results.append((o.cpu().numpy(), l.cpu().numpy(), dc.k.cpu().numpy(), dc.v.cpu().numpy()))
+    for a, b in zip(results[0], results[1]):
+        assert a.tobytes() == b.tobytes()
+    k2, v2 = pa.kv_append(case.k_pool[0], case.v_pool[0], kn, vn, case.block_tables, start, cu)
+    assert results[0][2].view(np.uint16).tobytes() == k2.tobytes()
+    assert results[0][3].view(np.uint16).tobytes() == v2.tobytes()
+    want = pa.paged_decode(case.q[0], k2, v2, case.block_tables, case.context_lens, case.scale,
+                           "bf16")
+    assert_parity((results[0][0].astype(np.float64), results[0][1].astype(np.float64)), want,
+                  "bf16", f"append+shared P{P}")
+    assert_no_device_error()
