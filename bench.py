@@ -32,7 +32,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_high_concurrency.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", "paged_decode.hip")
+# the sources of the first pass's translation unit; counters taken on other sources are
+# not reported
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
+               for f in ("paged_decode.hip", "common.h", "append_row.h", "mfma_tile.h")]
+
+
+def decode_source_digest():
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def parse_args():
@@ -95,8 +105,7 @@ def traffic_from_profile():
     """HBM bytes per launch from committed PMC counters, if taken on this kernel source."""
     try:
         info = json.load(open(TRAFFIC_FILE))
-        digest = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if info.get("kernel_source_sha256") == digest:
+        if info.get("kernel_source_sha256") == decode_source_digest():
             return info.get("bytes_per_launch")
     except (OSError, ValueError):
         pass

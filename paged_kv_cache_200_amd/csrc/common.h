@@ -10,6 +10,13 @@ namespace pkv {
 
 constexpr int kBlockTokens = 16;  // tokens per cache block (spindle, "Paging")
 constexpr int kWave = 64;         // CDNA wavefront width
+constexpr float kLn2 = 0.69314718055994530942f;
+// Online softmax: the running max (log2 units) is raised only when a score exceeds it
+// by more than this, so the rescale stays off the common path and every exponential
+// stays <= 2^8.
+constexpr float kLazyMaxSlack = 8.0f;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // bfloat16 halves of a packed 32-bit word, widened exactly to float32.
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

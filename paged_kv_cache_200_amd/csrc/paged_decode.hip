@@ -34,14 +34,13 @@
 PKV_DEFINE_ERROR_WORD(decode)
 
 #include "append_row.h"
+#include "mfma_tile.h"
 
 namespace pkv {
 namespace {
 
 constexpr int kLanesPerToken = 8;
 constexpr int kGroups = kWave / kLanesPerToken;  // token groups per wave
-constexpr float kLazyMaxSlack = 8.0f;            // log2 units
-constexpr float kLn2 = 0.69314718055994530942f;
 
 template <typename T, int D>
 struct Geom {
@@ -105,7 +104,6 @@ struct GroupState {
   float acc[G][Geom<T, D>::kElems]; // sum of exp2(score - m) * V over this lane's dims
 };
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // K/V that are read exactly once per call go through non-temporal 16-byte loads, which
 // keep the stream from displacing other data in the caches (measured ~10% more HBM
@@ -666,11 +664,12 @@ struct SeqUnits {
   int n, base, nsp, full, tail, tail_len;
 };
 
-__device__ __forceinline__ int group_of(const PlanInput& in, int s) {
-  int lo = 0, hi = in.num_groups;  // largest g with group_starts[g] <= s
+// Largest g with starts[g] <= s; `starts` is the group start array or its LDS copy.
+__device__ __forceinline__ int group_of(const int32_t* starts, int num_groups, int s) {
+  int lo = 0, hi = num_groups;
   while (hi - lo > 1) {
     const int mid = (lo + hi) / 2;
-    if (in.group_starts[mid] <= s) lo = mid; else hi = mid;
+    if (starts[mid] <= s) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -680,13 +679,14 @@ __device__ __forceinline__ int shared_slots(int shared_tokens, int part_tokens) 
   return part_tokens > 0 ? (shared_tokens + part_tokens - 1) / part_tokens : 1;
 }
 
-__device__ __forceinline__ SeqUnits seq_units(const PlanInput& in, int s) {
+__device__ __forceinline__ SeqUnits seq_units(const PlanInput& in, int s,
+                                              const int32_t* starts) {
   SeqUnits u;
   int n = in.ctx[s];
   u.n = n < 0 ? 0 : min(n, in.cap);
   int shared = 0;
   if (in.group_starts != nullptr) {
-    const int g = group_of(in, s);
+    const int g = group_of(starts, in.num_groups, s);
     shared = shared_prefix_tokens(in.group_shared_blocks[g], in.max_shared_blocks,
                                   in.cap / kBlockTokens);
   }
@@ -714,14 +714,23 @@ __device__ __forceinline__ int unit_slot(const SeqUnits& u, int p) {
 // Writes plan entries {sequence, first token, end token, slot | kDirectFlag}, their count,
 // and per sequence the number of partial slots the combine must merge (0: the sequence's
 // only unit writes out / lse itself).
+// Group starts are searched in an LDS copy when they fit (one load wave instead of a
+// chain of dependent global loads per sequence).
+constexpr int kPlanLdsGroups = 2047;
+
 __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restrict__ plan_count,
                                            int* __restrict__ nslots, const PlanInput in) {
   __shared__ int s_cursor[kPlanBuckets];
   __shared__ int s_scan[kPlanThreads / kWave];
   __shared__ int s_full_total;
+  __shared__ int s_starts[kPlanLdsGroups + 1];
   const int tid = threadIdx.x;
   s_cursor[tid] = 0;
   if (tid == 0) s_full_total = 0;
+  const bool lds_starts = in.group_starts != nullptr && in.num_groups <= kPlanLdsGroups;
+  if (lds_starts)
+    for (int g = tid; g <= in.num_groups; g += kPlanThreads) s_starts[g] = in.group_starts[g];
+  const int32_t* starts = lds_starts ? s_starts : in.group_starts;
   __syncthreads();
   const int P = in.part_tokens;
   if (in.group_starts != nullptr) {  // groups must tile 0..batch-1 in order
@@ -735,13 +744,15 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
   auto key_of = [&](int len) {
     return min(kPlanBuckets - 1, ((len + kBlockTokens - 1) / kBlockTokens) >> in.key_shift);
   };
+  SeqUnits first = {0, 0, 0, 0, 0, 0};  // this thread's sequence of the first round
   for (int base = 0; base < in.batch; base += kPlanThreads) {
     const int s = base + tid;
     SeqUnits u = {0, 0, 0, 0, 0, 0};
     if (s < in.batch) {
       const int raw = in.ctx[s];
       if (raw < 0 || raw > in.cap) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
-      u = seq_units(in, s);
+      u = seq_units(in, s, starts);
+      if (base == 0) first = u;
       const int units = u.full + u.tail;
       const int covered = u.base + u.full * P + (u.tail ? u.tail_len : 0);
       if (covered < u.n) PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
@@ -764,7 +775,7 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
   if (tid == kPlanThreads - 1) *plan_count = s_full_total + incl;
   __syncthreads();
   for (int s = tid; s < in.batch; s += kPlanThreads) {
-    const SeqUnits u = seq_units(in, s);
+    const SeqUnits u = s == tid ? first : seq_units(in, s, starts);
     if (u.tail) {
       const int t0 = u.base + u.full * P;
       plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] =
@@ -894,338 +905,31 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(
   }
 }
 
-// Matrix-core version (bf16 cache).  The group's query rows, (member, query head) pairs,
-// 16 per tile, are attended together against each shared block, which is read once per
-// tile through the first member's table row: 16 x 16 score tiles S^T = K Q^T on the bf16
-// MFMA (16x16x32), then O += P V on the bf16 MFMA (16x16x16) with P carried as a sum
-// of two bf16 terms.  Four waves take the range's blocks round-robin, each with its
-// own online softmax per row, and are merged through LDS.  A member whose table row does
-// not hold the same block ids over its share of the range is attended separately through
-// its own row, so the result never depends on the sharing being real.
-//
-// Lane layouts (c = lane % 16, h = lane / 16):
-//   S^T tile: lane holds rows c, tokens 4h + r (r = 0..3) of the block.  Score step k
-//     contracts dims 32k .. 32k + 31, lane h-group taking 8 of them: K[token c][32k + 8h ..]
-//     and Q[row c][32k + 8h ..], so one load instruction reads 64 contiguous bytes of
-//     every token row.
-//   P V, output tile j: A = P[row c][tokens 4h .. 4h + 3] (the lane's own scores),
-//     B = V[tokens 4h .. 4h + 3][c * D/16 + j], so lane loads the D/16 contiguous dims
-//     c * D/16 .. of 4 tokens.
-//   O tile j: lane holds rows 4h + r, dim c * D/16 + j.
-constexpr int kMfmaRows = 16;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-template <int D>
-struct MfmaGeom {
-  static constexpr int kQkSteps = D / 32;   // 16x16x32 steps over the head dim
-  static constexpr int kTiles = D / 16;     // output tiles of 16 dims
-  static constexpr int kVWords = D / 32;    // 32-bit words of V per lane and token
-  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-};
-
-template <int D>
-struct MfmaBlock {
-  u32x4_t k[MfmaGeom<D>::kQkSteps];
-  uint32_t v[4][MfmaGeom<D>::kVWords];
-};
-
-template <int D>
-__device__ __forceinline__ void mfma_load_block(MfmaBlock<D>& b, const uint16_t* __restrict__ kt,
-                                                const uint16_t* __restrict__ vt, int c, int h) {
-  using Mg = MfmaGeom<D>;
-#pragma unroll
-  for (int k = 0; k < Mg::kQkSteps; ++k)
-    b.k[k] = *reinterpret_cast<const u32x4_t*>(kt + c * D + 32 * k + 8 * h);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint16_t* src = vt + (4 * h + k) * D + c * Mg::kTiles;
-    if constexpr (Mg::kVWords == 4) {
-      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b.v[k][j] = w[j];
-    } else {
-      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
-      b.v[k][0] = w[0];
-      b.v[k][1] = w[1];
-    }
-  }
-}
-
-// LDS of one row tile: per wave the members found not to share the leader's blocks, and
-// per wave and row the softmax state and the unnormalised output.
-template <int D>
-struct MfmaShared {
-  unsigned mismatch[kSharedWaves];
-  float m[kSharedWaves][kMfmaRows];
-  float l[kSharedWaves][kMfmaRows];
-  float4 o[kSharedWaves][kMfmaRows][D / 4];
-};
-
-// Attends the rows of the members selected by `take` (bit mi: sequence base + mi) over
-// tokens [tok0, min(n_mi, tok1)) through table row `lead_seq`, and writes row (s, h) to
-// dst_out[(s * Hq + h) * slots + slot] (D floats) and dst_lse[...] (nullable).
-//
-// check: also compare every selected member's block ids with the leader's over the
-// member's share of the range (in the same loads that fetch the leader's ids).  Members
-// that differ come back as the result; if there are any, nothing is written and the
-// caller redoes the others without them and each of them through its own row.  Called
-// by all threads of the workgroup (it synchronises).
-template <int D, int G>
-__device__ __forceinline__ unsigned mfma_tile(
-    MfmaShared<D>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
-    const int32_t* __restrict__ ctx_lens, int lead_seq, int base, unsigned take, bool check,
-    int kvh, int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int tok0,
-    int tok1, int slot, int slots, float* __restrict__ dst_out, float* __restrict__ dst_lse) {
-  using Mg = MfmaGeom<D>;
-  constexpr int kMembers = kMfmaRows / G;
-  constexpr int kRows = kMembers * G;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave;
-  const int c = lane % 16;
-  const int h = lane / 16;
-  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
-  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
-  const int b0 = tok0 / kBlockTokens;
-  const int cap = W * kBlockTokens;
-  const int32_t* lead = tables + static_cast<size_t>(lead_seq) * W;
-
-  // Token limit of each selected member (uniform), the largest, and this lane's row's.
-  int nmem[kMembers];
-  int n_max = 0;
-  int n_c = 0;
-#pragma unroll
-  for (int mi = 0; mi < kMembers; ++mi) {
-    int n = 0;
-    if ((take >> mi) & 1u) {
-      n = ctx_lens[base + mi];
-      n = n < 0 ? 0 : min(min(n, cap), tok1);
-    }
-    nmem[mi] = n;
-    n_max = max(n_max, n);
-    if (c < kRows && c / G == mi) n_c = n;
-  }
-
-  // Query rows as the B operand of the score step (zero for rows not taken).
-  u32x4_t qr[Mg::kQkSteps];
-#pragma unroll
-  for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = u32x4_t{0u, 0u, 0u, 0u};
-  if (c < kRows && ((take >> (c / G)) & 1u)) {
-    const uint16_t* qrow =
-        q + (static_cast<size_t>(base + c / G) * num_q_heads + kvh * G + c % G) * D + 8 * h;
-#pragma unroll
-    for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
-  }
-
-  float m_c = -INFINITY;  // running max of row c, log2 units (lazy, as in the first pass)
-  float l_part = 0.0f;    // this lane's share of row c's exp-sum
-  f32x4_t o[Mg::kTiles];
-#pragma unroll
-  for (int j = 0; j < Mg::kTiles; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int nblk = n_max > tok0 ? (n_max - tok0 + kBlockTokens - 1) / kBlockTokens : 0;
-  const int nw = nblk > wave ? (nblk - wave + kSharedWaves - 1) / kSharedWaves : 0;
-  unsigned mism = 0;  // members whose ids differ on this wave's blocks
-  // Block ids of this wave's blocks, 64 at a time, one per lane.
-  int id_base = 0;
-  auto fetch_ids = [&](int from) -> int {
-    const int k = from + lane;
-    const bool live = k < nw;
-    const int b = b0 + wave + kSharedWaves * k;
-    int id = live ? lead[b] : 0;
-    if (check) {
-#pragma unroll
-      for (int mi = 0; mi < kMembers; ++mi) {
-        const bool differs = live && b * kBlockTokens < nmem[mi] &&
-                             tables[static_cast<size_t>(base + mi) * W + b] != id;
-        if (__any(differs)) mism |= 1u << mi;
-      }
-    }
-    const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
-    id = bad ? 0 : id;
-    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-    return id;
-  };
-  int ids = fetch_ids(0);
-  auto load = [&](MfmaBlock<D>& bl, int k) {  // called with k = 0, 1, 2, ... in order
-    if (k - id_base >= kWave) {
-      id_base += kWave;
-      ids = fetch_ids(id_base);
-    }
-    const int id = __builtin_amdgcn_readlane(ids, k - id_base);
-    const size_t off = static_cast<size_t>(id) * block_elems + kvh * head_elems;
-    mfma_load_block<D>(bl, kc + off, vc + off, c, h);
-  };
-  auto process = [&](MfmaBlock<D>& cur, int k) {
-    const int t_base = (b0 + wave + kSharedWaves * k) * kBlockTokens;  // token of slot 0
-    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < Mg::kQkSteps; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
-                                                   __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
-                                                   0);
-    // Scores of row c for tokens 4h + i, masked by the row's own length (select, so
-    // stale or NaN slots never pass).
-    float x[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, x[i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const bool raise = bm > m_c + kLazyMaxSlack;
-    if (__any(raise)) {
-      float a = 1.0f;
-      if (raise) {
-        a = m_c == -INFINITY ? 0.0f : fast_exp2(m_c - bm);
-        m_c = bm;
-      }
-      l_part *= a;
-      // Output rows 4h + i take the factor of the lanes that own score row 4h + i.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(a, 4 * h + i);
-#pragma unroll
-        for (int j = 0; j < Mg::kTiles; ++j) o[j][i] *= ai;
-      }
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - m_c);
-      l_part += p[i];
-    }
-    // P V on the bf16 MFMA with P split into two bf16 terms, hi = P truncated and
-    // lo = (P - hi) truncated (P - hi is exact in fp32), so the product sees P to about
-    // 2^-16 relative.  A operand: P[row c][tokens 4h .. 4h + 3], the lane's own scores.
-    uint32_t hb[4], lb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hb[i] = __float_as_uint(p[i]) & 0xffff0000u;
-      lb[i] = __float_as_uint(p[i] - __uint_as_float(hb[i])) & 0xffff0000u;
-    }
-    const i16x4_t a_hi = __builtin_bit_cast(
-        i16x4_t, u32x2_t{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3]});
-    const i16x4_t a_lo = __builtin_bit_cast(
-        i16x4_t, u32x2_t{(lb[0] >> 16) | lb[1], (lb[2] >> 16) | lb[3]});
-    // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
-    if (t_base + kBlockTokens > n_max) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool vok = t_base + 4 * h + i < n_max;
-#pragma unroll
-        for (int w = 0; w < Mg::kVWords; ++w) cur.v[i][w] = vok ? cur.v[i][w] : 0u;
-      }
-    }
-    const auto& v = cur.v;
-    // B operand of tile j: V[tokens 4h .. 4h + 3][dim c * D/16 + j], the even tiles from
-    // the low halves of the lane's words, the odd ones from the high halves.
-#pragma unroll
-    for (int w = 0; w < Mg::kVWords; ++w) {
-      const i16x4_t b_even = __builtin_bit_cast(
-          i16x4_t, u32x2_t{(v[0][w] & 0xffffu) | (v[1][w] << 16),
-                           (v[2][w] & 0xffffu) | (v[3][w] << 16)});
-      const i16x4_t b_odd = __builtin_bit_cast(
-          i16x4_t, u32x2_t{(v[0][w] >> 16) | (v[1][w] & 0xffff0000u),
-                           (v[2][w] >> 16) | (v[3][w] & 0xffff0000u)});
-      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_even, o[2 * w], 0, 0, 0);
-      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_even, o[2 * w], 0, 0, 0);
-      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_odd, o[2 * w + 1], 0, 0, 0);
-      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_odd, o[2 * w + 1], 0, 0, 0);
-    }
-  };
-  // Two blocks in flight: the next block's loads are issued before this one's math.
-  MfmaBlock<D> bufa, bufb;
-  if (nw > 0) load(bufa, 0);
-  for (int k = 0; k < nw; k += 2) {
-    if (k + 1 < nw) load(bufb, k + 1);
-    process(bufa, k);
-    if (k + 1 < nw) {
-      if (k + 2 < nw) load(bufa, k + 2);
-      process(bufb, k + 1);
-    }
-  }
-  float l_c = l_part;
-  l_c += __shfl_xor(l_c, 16);
-  l_c += __shfl_xor(l_c, 32);
-
-  // Merge the waves: each publishes (m, l) per row and its unnormalised rows.
-  constexpr int kQuads = Mg::kTiles / 4;  // float4s per lane and row
-  if (h == 0) {
-    sm.m[wave][c] = m_c;
-    sm.l[wave][c] = l_c;
-  }
-  if (lane == 0) sm.mismatch[wave] = mism;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int u = 0; u < kQuads; ++u)
-      sm.o[wave][4 * h + i][c * kQuads + u] =
-          make_float4(o[4 * u][i], o[4 * u + 1][i], o[4 * u + 2][i], o[4 * u + 3][i]);
-  }
-  __syncthreads();
-  unsigned differ = 0;
-#pragma unroll
-  for (int w = 0; w < kSharedWaves; ++w) differ |= sm.mismatch[w];
-  differ &= take;
-  // A member that does not share streamed the leader's blocks up to its own length,
-  // which can include slots stale for everyone (NaN V times a zero weight spoils every
-  // row), so a tile with any such member writes nothing and is redone without it.
-  const unsigned write = differ != 0 ? 0u : take;
-  const int row = tid / 16;  // 16 rows x 16 threads of D/16 dims
-  const int cc = tid % 16;
-  const int mi = row / G;
-  if (row < kRows && ((write >> mi) & 1u)) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kSharedWaves; ++w) M = fmaxf(M, sm.m[w][row]);
-    float e[kSharedWaves];
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kSharedWaves; ++w) {
-      e[w] = sm.m[w][row] == -INFINITY ? 0.0f : fast_exp2(sm.m[w][row] - M);
-      L += sm.l[w][row] * e[w];
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const size_t sh = static_cast<size_t>(base + mi) * num_q_heads + kvh * G + row % G;
-    float* dst = dst_out + (sh * slots + slot) * D + cc * Mg::kTiles;
-#pragma unroll
-    for (int u = 0; u < kQuads; ++u) {
-      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-      for (int w = 0; w < kSharedWaves; ++w) {
-        const float4 x = sm.o[w][row][cc * kQuads + u];
-        acc.x = fmaf(e[w], x.x, acc.x);
-        acc.y = fmaf(e[w], x.y, acc.y);
-        acc.z = fmaf(e[w], x.z, acc.z);
-        acc.w = fmaf(e[w], x.w, acc.w);
-      }
-      acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-      // dims cc * D/16 + j of tile j: float4 u holds tiles 4u .. 4u + 3
-      *reinterpret_cast<float4*>(dst + 4 * u) = acc;
-    }
-    if (cc == 0 && dst_lse != nullptr)
-      dst_lse[sh * slots + slot] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();  // LDS reused by the next call
-  return differ;
-}
-
 // One launch for a batch of fork groups: workgroups [0, shared_wgs) are (shared partition,
 // KV head, group) = (x % nsp, x / nsp % Hkv, x / (nsp * Hkv)); the rest take the plan's
 // units (each sequence's private range, and whole sequences of groups that share nothing),
 // unit (x - shared_wgs) / Hkv for KV head (x - shared_wgs) % Hkv, as one-member tiles
 // through the member's own table row.  The private units' short latency chains overlap
 // the shared stream instead of following it.
+// Token limits of members base .. base + kMembers - 1 of a decode tile: each member's
+// context length clamped to the table and to `tok1`, 0 for members not taken.
+template <int G>
+__device__ __forceinline__ void decode_limits(int (&lim)[kMfmaRows / G],
+                                              const int32_t* __restrict__ ctx_lens, int base,
+                                              unsigned take, int cap, int tok1) {
+#pragma unroll
+  for (int mi = 0; mi < kMfmaRows / G; ++mi) {
+    int n = 0;
+    if ((take >> mi) & 1u) {
+      n = ctx_lens[base + mi];
+      n = n < 0 ? 0 : min(min(n, cap), tok1);
+    }
+    lim[mi] = n;
+  }
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kernel(
+__global__ __launch_bounds__(kTileWaves * kWave) void decode_shared_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ group_starts,
@@ -1236,17 +940,21 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kerne
     const int4* __restrict__ plan, const int* __restrict__ plan_count) {
   constexpr int kMembers = kMfmaRows / G;  // members per row tile
   __shared__ MfmaShared<D> sm;
+  const int cap = W * kBlockTokens;
   const int shared_wgs = nsp_grid * num_kv_heads * num_groups;
   const int x = blockIdx.x;
+  int lim[kMembers];
   if (x >= shared_wgs) {
     const int u = (x - shared_wgs) / num_kv_heads;
     const int kvh = (x - shared_wgs) % num_kv_heads;
     if (u >= *plan_count) return;
     const int4 e = plan[u];
     const bool direct = (e.w & kDirectFlag) != 0;
-    mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, e.x, e.x, 1u, false, kvh, num_q_heads,
-                    num_kv_heads, num_blocks, scale_log2, e.y, e.z, direct ? 0 : e.w & kSlotMask,
-                    direct ? 1 : max_parts, direct ? out : part_out, direct ? lse : part_lse);
+    decode_limits<G>(lim, ctx_lens, e.x, 1u, cap, e.z);
+    mfma_tile<D, G>(sm, q, kc, vc, tables + static_cast<size_t>(e.x) * W, nullptr, W, lim, 1u,
+                    e.x, kvh, num_q_heads, num_kv_heads, num_blocks, scale_log2, e.y,
+                    direct ? 0 : e.w & kSlotMask, direct ? 1 : max_parts,
+                    direct ? out : part_out, direct ? lse : part_lse);
     return;
   }
   const int part = x % nsp_grid;
@@ -1256,22 +964,24 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_mfma_kerne
   if (!r.live) return;
   for (int base = r.m0; base < r.m1; base += kMembers) {
     const int cnt = min(kMembers, r.m1 - base);
+    const unsigned all = (1u << cnt) - 1u;
+    const int32_t* rows = tables + static_cast<size_t>(base) * W;
+    decode_limits<G>(lim, ctx_lens, base, all, cap, r.tok1);
     // The tile's members through the first one's row; if the sharing hint was wrong for
     // some, the others again without them, then each of them through its own row.
-    const unsigned all = (1u << cnt) - 1u;
-    unsigned differ = mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, base, base, all, true,
-                                      kvh, num_q_heads, num_kv_heads, num_blocks, scale_log2,
-                                      r.tok0, r.tok1, part, max_parts, part_out, part_lse);
+    unsigned differ = mfma_tile<D, G>(sm, q, kc, vc, rows, rows, W, lim, all, base, kvh,
+                                      num_q_heads, num_kv_heads, num_blocks, scale_log2, r.tok0,
+                                      part, max_parts, part_out, part_lse);
     if (differ != 0 && (all & ~differ) != 0)
-      mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, base, base, all & ~differ, false, kvh,
-                      num_q_heads, num_kv_heads, num_blocks, scale_log2, r.tok0, r.tok1, part,
-                      max_parts, part_out, part_lse);
+      mfma_tile<D, G>(sm, q, kc, vc, rows, nullptr, W, lim, all & ~differ, base, kvh,
+                      num_q_heads, num_kv_heads, num_blocks, scale_log2, r.tok0, part, max_parts,
+                      part_out, part_lse);
     while (differ != 0) {
       const int mi = __builtin_ctz(differ);
       differ &= differ - 1u;
-      mfma_tile<D, G>(sm, q, kc, vc, tables, W, ctx_lens, base + mi, base, 1u << mi, false, kvh,
-                      num_q_heads, num_kv_heads, num_blocks, scale_log2, r.tok0, r.tok1, part,
-                      max_parts, part_out, part_lse);
+      mfma_tile<D, G>(sm, q, kc, vc, rows + static_cast<size_t>(mi) * W, nullptr, W, lim,
+                      1u << mi, base, kvh, num_q_heads, num_kv_heads, num_blocks, scale_log2,
+                      r.tok0, part, max_parts, part_out, part_lse);
     }
   }
 }
@@ -1342,8 +1052,8 @@ using SharedFn = bool (*)(const SharedArgs&, hipStream_t);
 
 template <typename T, int D, int G>
 bool shared_launch(const SharedArgs& a, hipStream_t stream) {
-  const dim3 block(kSharedWaves * kWave);
   if constexpr (sizeof(T) == 2) {
+    const dim3 block(kTileWaves * kWave);
     const int groups = a.nsp > 0 ? a.num_groups : 0;
     const long long wgs = static_cast<long long>(a.nsp) * a.hkv * groups +
                           static_cast<long long>(a.batch) * a.max_slots * a.hkv;
@@ -1356,6 +1066,7 @@ bool shared_launch(const SharedArgs& a, hipStream_t stream) {
                        a.lse, a.plan, a.plan_count);
     return true;
   } else {
+    const dim3 block(kSharedWaves * kWave);
     if (a.nsp > 0)
       hipLaunchKernelGGL((decode_shared_kernel<T, D, G>), dim3(a.nsp, a.hkv, a.num_groups), block,
                          0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.kc),
