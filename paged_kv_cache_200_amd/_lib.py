@@ -1,4 +1,5 @@
-"""ctypes declarations of libpkv.so (include/pkv.h, include/pkv_block_manager.h).
+"""ctypes declarations of libpkv.so (include/pkv.h, include/pkv_block_manager.h,
+include/pkv_replay.h).
 
 The library must have been built (``python -m paged_kv_cache_200_amd.build``);
 there is no fallback: importing the ops without it raises.  torch is imported
@@ -84,7 +85,16 @@ SIGNATURES = {
     "pkv_bm_refcount": (ctypes.c_int, [_vp, _i32, _pi32]),
     "pkv_bm_num_free": (ctypes.c_int, [_vp, _pi32]),
     "pkv_bm_free_list": (ctypes.c_int, [_vp, _pi32, _i32, _pi32]),
+    "pkv_replay_allocator": (ctypes.c_int, [_i32, _i32, _pi32, _pi32, _i32, _i32, _i32, _vp,
+                                            _vp, _pi32, _i32, _vp]),
 }
+
+
+class ReplayResultC(ctypes.Structure):
+    """pkv_replay_result (include/pkv_replay.h)."""
+
+    _fields_ = [("peak_slots", ctypes.c_int64), ("mean_utilisation", ctypes.c_double),
+                ("steps", ctypes.c_int32), ("preemptions", ctypes.c_int32)]
 
 
 class PkvError(RuntimeError):

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["paged_decode.hip", "kv_append.hip", "copy_blocks.hip", "status.hip"]
-HOST_SOURCES = ["block_manager.cpp"]
+HOST_SOURCES = ["block_manager.cpp", "replay.cpp"]
 
 
 def _hipcc() -> str:

@@ -2,12 +2,13 @@
 (no GPU needed; nothing here launches a kernel)."""
 
 import ctypes
+import glob
 import os
 import re
 
 from libpkv_util import ROOT, ensure_built
 
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pkv.h", "pkv_block_manager.h")]
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 DECL = re.compile(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(pkv_[a-z0-9_]+)\s*\(", re.M)
 
 

@@ -443,3 +443,18 @@ def replay_step_values(sched: ReplaySchedule, step: int, layer: int, seqs, kind:
     k = parallel_normal(ks, (T, sched.num_kv_heads, sched.head_dim))
     v = parallel_normal(vs, (T, sched.num_kv_heads, sched.head_dim))
     return k, v
+
+
+# --------------------------------------------------------------------------------------
+# Allocator replay: 64 requests through an 8192-slot cache with 16-token blocks, prompt
+# and generation lengths drawn as in the GPT-2 replay; max_new_tokens 192 (the bound a
+# contiguous buffer must be sized for at admission).
+# --------------------------------------------------------------------------------------
+
+def allocator_replay_requests(seed: int = 0, n: int = 64):
+    """(prompt_lens, gen_lens) int32 [n] and the settings of the replay."""
+    st = _streams(seed)
+    rng = np.random.default_rng(st["lengths"])
+    prompts = rng.integers(16, 129, size=n).astype(np.int32)
+    gens = _lognormal_lengths(rng, n, 48, 0.75, 192)
+    return prompts, gens, dict(max_new_tokens=192, total_slots=8192, block_size=16)
