@@ -35,184 +35,10 @@ PKV_DEFINE_ERROR_WORD(decode)
 
 #include "append_row.h"
 #include "mfma_tile.h"
+#include "valu_attend.h"
 
 namespace pkv {
 namespace {
-
-constexpr int kLanesPerToken = 8;
-constexpr int kGroups = kWave / kLanesPerToken;  // token groups per wave
-
-template <typename T, int D>
-struct Geom {
-  static constexpr int kChunkElems = 16 / static_cast<int>(sizeof(T));  // elems per 16 B
-  static constexpr int kChunks = D * static_cast<int>(sizeof(T)) / (16 * kLanesPerToken);
-  static constexpr int kElems = kChunks * kChunkElems;                   // elems per lane
-  static constexpr int kWords = kChunks * 4;                             // 32-bit words per lane
-  static constexpr int kChunkStride = kLanesPerToken * kChunkElems;     // elems between chunks
-  static_assert(kChunks >= 1, "head_dim too small for 8 lanes per token");
-};
-
-// Dimension held by element e of a lane with sub-index `sub` (0..7).
-template <typename T, int D>
-__device__ __forceinline__ int lane_dim(int sub, int e) {
-  using Gm = Geom<T, D>;
-  return (e / Gm::kChunkElems) * Gm::kChunkStride + sub * Gm::kChunkElems + (e % Gm::kChunkElems);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-template <typename T>
-__device__ __forceinline__ float dot_word(uint32_t qw, uint32_t kw, float acc);
-
-template <>
-__device__ __forceinline__ float dot_word<uint16_t>(uint32_t qw, uint32_t kw, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw),
-                                         __builtin_bit_cast(bf16x2_t, kw), acc, false);
-}
-
-template <>
-__device__ __forceinline__ float dot_word<float>(uint32_t qw, uint32_t kw, float acc) {
-  return fmaf(__uint_as_float(qw), __uint_as_float(kw), acc);
-}
-
-// Widen the words of one token's chunks to float32 values, in element order.
-template <typename T, int D>
-__device__ __forceinline__ void widen(const uint32_t (&w)[Geom<T, D>::kWords],
-                                      float (&v)[Geom<T, D>::kElems]) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int j = 0; j < Geom<T, D>::kWords; ++j) {
-      v[2 * j] = bf16_lo(w[j]);
-      v[2 * j + 1] = bf16_hi(w[j]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < Geom<T, D>::kWords; ++j) v[j] = __uint_as_float(w[j]);
-  }
-}
-
-template <typename T, int D>
-struct TokenRegs {
-  uint32_t k[2][Geom<T, D>::kWords];  // [token in block: grp, grp+8][words]
-  uint32_t v[2][Geom<T, D>::kWords];
-};
-
-template <typename T, int D, int G>
-struct GroupState {
-  float m[G];                       // lazy running max, log2 units
-  float l[G];                       // sum of exp2(score - m)
-  float acc[G][Geom<T, D>::kElems]; // sum of exp2(score - m) * V over this lane's dims
-};
-
-
-// K/V that are read exactly once per call go through non-temporal 16-byte loads, which
-// keep the stream from displacing other data in the caches (measured ~10% more HBM
-// throughput on gfx950 for random 4 KiB tiles than plain loads).  Blocks shared by
-// several sequences are read with plain loads so sibling waves find them cached.
-template <bool kStreaming>
-__device__ __forceinline__ u32x4_t load16(const void* p) {
-  if constexpr (kStreaming)
-    return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
-  else
-    return *static_cast<const u32x4_t*>(p);
-}
-
-template <typename T, int D, bool kStreaming>
-__device__ __forceinline__ void load_block(TokenRegs<T, D>& r, const T* __restrict__ kt,
-                                           const T* __restrict__ vt, int lane_off) {
-  using Gm = Geom<T, D>;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int c = 0; c < Gm::kChunks; ++c) {
-      const int off = lane_off + i * kGroups * D + c * Gm::kChunkStride;
-      const u32x4_t kk = load16<kStreaming>(kt + off);
-      const u32x4_t vv = load16<kStreaming>(vt + off);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r.k[i][4 * c + j] = kk[j];
-        r.v[i][4 * c + j] = vv[j];
-      }
-    }
-  }
-}
-
-// One 16-token block: 2 tokens per lane (token grp and grp + 8 of the block).
-// kMasked: only the first n_valid tokens of the block count.
-template <typename T, int D, int G, bool kMasked>
-__device__ __forceinline__ void process_block(const TokenRegs<T, D>& r,
-                                              const uint32_t (&q)[G][Geom<T, D>::kWords],
-                                              GroupState<T, D, G>& st, float scale_log2,
-                                              int grp, int n_valid) {
-  using Gm = Geom<T, D>;
-  float sc[2][G];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float a = 0.0f;
-#pragma unroll
-      for (int j = 0; j < Gm::kWords; ++j) a = dot_word<T>(q[g][j], r.k[i][j], a);
-      sc[i][g] = a;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) sc[i][g] = group8_sum(sc[i][g]) * scale_log2;
-  }
-  bool valid[2] = {true, true};
-  if constexpr (kMasked) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      valid[i] = (i * kGroups + grp) < n_valid;
-#pragma unroll
-      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? sc[i][g] : -INFINITY;
-    }
-  }
-  bool raise = false;
-#pragma unroll
-  for (int g = 0; g < G; ++g) raise |= fmaxf(sc[0][g], sc[1][g]) > st.m[g] + kLazyMaxSlack;
-  if (raise) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mn = fmaxf(st.m[g], fmaxf(sc[0][g], sc[1][g]));
-      const float a = (st.m[g] == -INFINITY) ? 0.0f : fast_exp2(st.m[g] - mn);
-      st.l[g] *= a;
-#pragma unroll
-      for (int e = 0; e < Gm::kElems; ++e) st.acc[g][e] *= a;
-      st.m[g] = mn;
-    }
-  }
-  float p[2][G];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float e = fast_exp2(sc[i][g] - st.m[g]);
-      p[i][g] = (kMasked && !valid[i]) ? 0.0f : e;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) st.l[g] += p[0][g] + p[1][g];
-  float v0[Gm::kElems], v1[Gm::kElems];
-  widen<T, D>(r.v[0], v0);
-  widen<T, D>(r.v[1], v1);
-  if constexpr (kMasked) {
-    // select, not multiply: stale or NaN slots must not reach the accumulator
-#pragma unroll
-    for (int e = 0; e < Gm::kElems; ++e) {
-      v0[e] = valid[0] ? v0[e] : 0.0f;
-      v1[e] = valid[1] ? v1[e] : 0.0f;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int e = 0; e < Gm::kElems; ++e)
-      st.acc[g][e] = fmaf(p[1][g], v1[e], fmaf(p[0][g], v0[e], st.acc[g][e]));
-  }
-}
 
 // Log-sum-exp merge of one (sequence, query head)'s partition results, by one wavefront:
 // lane p holds partition p's log-sum-exp (64 partitions per round), so the max and the
@@ -307,134 +133,6 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
                  part_out + sh * max_parts * D, nparts, lane);
 }
 
-// One wave's share of a unit: attend this KV head's G query rows of sequence s over the
-// tokens [tok0, tok1) (tok0 a multiple of the block size, tok0 <= tok1), taking the range's full blocks wave, wave + NW, ... (and the trailing
-// partial block if it falls to this wave), then merge the wave's 8 token groups so that
-// every lane holds the wave's totals (m, l, acc) for its dims.
-template <typename T, int D, int G, int NW, int DEPTH, bool kStreaming>
-__device__ __forceinline__ void attend_range(GroupState<T, D, G>& st, const T* __restrict__ q,
-                                             const T* __restrict__ kc, const T* __restrict__ vc,
-                                             const int32_t* __restrict__ tables, int W, int s,
-                                             int kvh, int num_q_heads, int num_kv_heads,
-                                             int num_blocks, float scale_log2, int tok0,
-                                             int tok1, int wave, int lane) {
-  using Gm = Geom<T, D>;
-  const int grp = lane / kLanesPerToken;
-  const int sub = lane % kLanesPerToken;
-  // Query rows of this KV head's group, this lane's dims, raw bits.
-  uint32_t qr[G][Gm::kWords];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const T* qrow = q + (static_cast<size_t>(s) * num_q_heads + kvh * G + g) * D;
-#pragma unroll
-    for (int c = 0; c < Gm::kChunks; ++c) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qrow + c * Gm::kChunkStride +
-                                                      sub * Gm::kChunkElems);
-      qr[g][4 * c + 0] = w.x; qr[g][4 * c + 1] = w.y;
-      qr[g][4 * c + 2] = w.z; qr[g][4 * c + 3] = w.w;
-    }
-  }
-
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.m[g] = -INFINITY;
-    st.l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < Gm::kElems; ++e) st.acc[g][e] = 0.0f;
-  }
-
-  const int b_begin = tok0 / kBlockTokens;
-  const int nfull = tok1 / kBlockTokens - b_begin;  // blocks wholly inside [tok0, tok1)
-  const int tail = tok1 % kBlockTokens;             // valid tokens of a trailing partial block
-  const int nfull_w = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
-
-  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
-  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
-  const T* kbase = kc + kvh * head_elems;
-  const T* vbase = vc + kvh * head_elems;
-  const int lane_off = grp * D + sub * Gm::kChunkElems;
-  const int32_t* trow = tables + static_cast<size_t>(s) * W;
-
-  // Block ids of this wave's full blocks, 64 at a time, one per lane.
-  int id_base = 0;
-  auto fetch_ids = [&](int base) -> int {
-    const int k = base + lane;
-    int id = 0;
-    bool bad = false;
-    if (k < nfull_w) {
-      id = trow[b_begin + wave + NW * k];
-      bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
-      id = bad ? 0 : id;
-    }
-    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-    return id;
-  };
-  int ids = fetch_ids(0);
-  auto block_of = [&](int k) -> int {  // called with k = 0, 1, 2, ... in order
-    if (k - id_base >= kWave) {
-      id_base += kWave;
-      ids = fetch_ids(id_base);
-    }
-    return __builtin_amdgcn_readlane(ids, k - id_base);
-  };
-  auto load = [&](TokenRegs<T, D>& r, int blk) {
-    load_block<T, D, kStreaming>(r, kbase + static_cast<size_t>(blk) * block_elems,
-                     vbase + static_cast<size_t>(blk) * block_elems, lane_off);
-  };
-
-  TokenRegs<T, D> rr[DEPTH];
-#pragma unroll
-  for (int j = 0; j + 1 < DEPTH; ++j)
-    if (j < nfull_w) load(rr[j], block_of(j));
-  for (int k = 0; k < nfull_w; k += DEPTH) {
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      if (k + j < nfull_w) {
-        const int ahead = k + j + DEPTH - 1;
-        if (ahead < nfull_w) load(rr[(j + DEPTH - 1) % DEPTH], block_of(ahead));
-        process_block<T, D, G, false>(rr[j], qr, st, scale_log2, grp, kBlockTokens);
-      }
-    }
-  }
-
-  // The trailing partial block (only in the partition holding the sequence end)
-  // goes to the wave next in the round-robin.
-  if (tail != 0 && wave == nfull % NW) {
-    int b = trow[b_begin + nfull];
-    if (static_cast<unsigned>(b) >= static_cast<unsigned>(num_blocks)) {
-      if (lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-      b = 0;
-    }
-    load(rr[0], b);
-    process_block<T, D, G, true>(rr[0], qr, st, scale_log2, grp, tail);
-  }
-
-  // Merge the 8 token groups of the wave (lanes with equal `sub` hold the same dims).
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float mx = st.m[g];
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float a = (st.m[g] == -INFINITY) ? 0.0f : fast_exp2(st.m[g] - mx);
-    float l = st.l[g] * a;
-    l += __shfl_xor(l, 8);
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    st.l[g] = l;
-#pragma unroll
-    for (int e = 0; e < Gm::kElems; ++e) {
-      float x = st.acc[g][e] * a;
-      x += __shfl_xor(x, 8);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      st.acc[g][e] = x;
-    }
-    st.m[g] = mx;
-  }
-
-}
-
 // Grid layouts of the first pass.
 //   kOrderPartMinor: x = partition, y = KV-head group, z = sequence.
 //   kOrderPartMajorReversed: x = KV-head group, y = sequence, z = partition counted from
@@ -511,7 +209,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
   const int lane = threadIdx.x % kWave;
 
   GroupState<T, D, G> st;
-  attend_range<T, D, G, NW, DEPTH, true>(st, q, kc, vc, tables, W, s, kvh, num_q_heads,
+  attend_range<T, D, G, NW, DEPTH, true>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
                                          num_kv_heads, num_blocks, scale_log2, tok0, tok1, wave,
                                          lane);
   const int grp = lane / kLanesPerToken;
@@ -835,7 +533,7 @@ __device__ __forceinline__ void shared_member(
   // the block boundary tok0 (attend_range needs a block-aligned start).
   const int t1 = max(tok0, min(tok1, n));
   GroupState<T, D, G> st;
-  attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, kvh, num_q_heads,
+  attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
                                      num_kv_heads, num_blocks, scale_log2, tok0, t1, 0, lane);
   if (grp != 0) return;
 #pragma unroll
