@@ -257,6 +257,35 @@ int pkv_append_paged_decode_shared_prefix(
     pkv_stream_t stream);
 
 /*
+ * Paged (chunked) prefill attention (spindle, "Why write the forward pass":
+ * the prompt runs through the same forward pass over the block cache;
+ * "Two bugs worth recording": explicit positions and lengths).  Sequence s
+ * owns query rows cu_q[s] .. cu_q[s+1]-1 of q; they are the LAST
+ * q_len = cu_q[s+1] - cu_q[s] tokens of its context of context_lens[s]
+ * tokens, whose K/V must already be in the cache (pkv_kv_append first).
+ * Query i attends causally to tokens [0, context_lens[s] - q_len + i].
+ *
+ *   out : float32 [total_q][num_q_heads][head_dim]   (16-byte aligned)
+ *   lse : float32 [total_q][num_q_heads], natural log; may be NULL
+ *   q   : [total_q][num_q_heads][head_dim] in the cache dtype
+ *   cu_q: int32 [batch + 1], non-decreasing, cu_q[0] = 0, cu_q[batch] = total_q
+ *   max_q_len : host bound on every chunk's length (grid size)
+ * Caches, tables, head and block sizes as in pkv_paged_decode.  bf16 caches
+ * run on the matrix cores (16 (token, head) rows of one sequence per tile),
+ * fp32 caches on the VALU (one wave per query token).  One launch; no
+ * workspace.  Device-side violations (cu_q malformed, a chunk longer than
+ * its context or than max_q_len, context beyond the table, bad block ids)
+ * set PKV_DEVERR_* bits; affected rows are then unspecified, every access
+ * stays in bounds.
+ */
+int pkv_paged_prefill(float* out, float* lse, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
+                      const int32_t* cu_q, const int32_t* context_lens, int32_t batch,
+                      int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, float scale, int32_t dtype, pkv_stream_t stream);
+
+/*
  * First pass only: per-partition attention, no merge.
  *   part_out : float32 [batch][num_q_heads][max_partitions][head_dim]
  *   part_lse : float32 [batch][num_q_heads][max_partitions]

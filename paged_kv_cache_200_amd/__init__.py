@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     paged_decode_partials,
     paged_decode_planned,
     paged_decode_shared_prefix,
+    paged_prefill,
     shared_prefix_workspace_bytes,
 )
 from .block_manager import BlockManager, OutOfBlocks  # noqa: F401

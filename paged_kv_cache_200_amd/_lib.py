@@ -66,6 +66,8 @@ SIGNATURES = {
                                                              _vp, _vp, _i32, _i32, _i32, _i32,
                                                              _i32, _i32, _i32, _i32, _i32, _f32,
                                                              _i32, _vp, _sz, _i32, _vp]),
+    "pkv_paged_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "pkv_paged_decode_partials": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                                  _i32, _i32, _vp, _i32, _vp]),

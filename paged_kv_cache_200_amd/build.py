@@ -24,7 +24,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["paged_decode.hip", "kv_append.hip", "copy_blocks.hip", "status.hip"]
+HIP_SOURCES = ["paged_decode.hip", "prefill.hip", "kv_append.hip", "copy_blocks.hip",
+               "status.hip"]
 HOST_SOURCES = ["block_manager.cpp", "replay.cpp"]
 
 

@@ -48,6 +48,11 @@ inline int launch_status() {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Scores are kept in log2 units: scale * log2(e), rounded once to float32.
+inline float scale_to_log2(float scale) {
+  return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+}
+
 inline int elem_bytes(int32_t dtype) {
   return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 0;
 }
@@ -58,6 +63,7 @@ inline int elem_bytes(int32_t dtype) {
 extern "C" int pkv_internal_take_error_decode(int32_t* flags);
 extern "C" int pkv_internal_take_error_append(int32_t* flags);
 extern "C" int pkv_internal_take_error_copy(int32_t* flags);
+extern "C" int pkv_internal_take_error_prefill(int32_t* flags);
 
 #define PKV_DEFINE_ERROR_WORD(NAME)                                                  \
   namespace {                                                                        \

@@ -835,10 +835,6 @@ int num_partitions(int32_t max_ctx, int32_t part_tokens) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-float scale_to_log2(float scale) {
-  return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
-}
-
 // Partitioning of one call.  Plain decode: P = ceil(max_context_len / partition_size)
 // partitions of partition_size tokens when that exceeds one (else one unit per sequence,
 // written straight).  Shared-prefix decode: a sequence's slots are the shared prefix's

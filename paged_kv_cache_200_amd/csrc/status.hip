@@ -26,5 +26,6 @@ extern "C" int pkv_device_error(pkv_stream_t stream, int32_t* flags) {
   int st = pkv_internal_take_error_decode(flags);
   if (st == PKV_OK) st = pkv_internal_take_error_append(flags);
   if (st == PKV_OK) st = pkv_internal_take_error_copy(flags);
+  if (st == PKV_OK) st = pkv_internal_take_error_prefill(flags);
   return st;
 }

@@ -285,6 +285,43 @@ def append_paged_decode_shared_prefix(q, k_cache, v_cache, k_new, v_new, block_t
     return out, lse
 
 
+def paged_prefill(q, k_cache, v_cache, block_tables, cu_q, context_lens, max_q_len,
+                  scale=None, out=None, lse=None, want_lse=True, stream=None):
+    """Causal attention of each sequence's newest chunk of query tokens over its paged
+    context (see pkv_paged_prefill).  q [T, Hq, D]; returns (out [T, Hq, D], lse [T, Hq])
+    float32.  The chunk's K/V must already be appended."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _gpu(t, n)
+    _same_kind(k_cache, q, "q")
+    _same_kind(k_cache, v_cache, "v_cache")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [T, Hq, D] and caches [NB, Hkv, 16, D] expected")
+    T, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    if k_cache.shape[2] != BLOCK_SIZE or k_cache.shape[3] != d:
+        raise ValueError("cache must be [num_blocks, num_kv_heads, 16, head_dim]")
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(cu_q, "cu_q", torch.int32)
+    _gpu(context_lens, "context_lens", torch.int32)
+    B = context_lens.shape[0]
+    if cu_q.shape != (B + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("cu_q [B + 1] and block_tables [B, W] expected")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    _gpu(out, "out", torch.float32)
+    if lse is None and want_lse:
+        lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+    _lib.call("pkv_paged_prefill", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+              _ptr(block_tables), block_tables.shape[1], _ptr(cu_q), _ptr(context_lens), B, T,
+              int(max_q_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale), _kv_code(k_cache),
+              _stream(stream))
+    return out, lse
+
+
 def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                           partition_size, scale=None, max_partitions=None, part_out=None,
                           part_lse=None, plan_workspace=None, stream=None):
