@@ -52,7 +52,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="high_concurrency",
                    choices=["high_concurrency", "long_context", "prefix_fork", "qwen_gqa", "tiny",
-                            "gpt2_replay"])
+                            "gpt2_replay", "chunked_prefill"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=None,
                    help="split-KV partition size in tokens (default: the workload's own, else "
@@ -150,6 +150,108 @@ def unique_kv_tokens(case):
             b = int(case.block_tables[s, j])
             valid[b] = max(valid.get(b, 0), min(16, n - 16 * j))
     return sum(valid.values())
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def run_prefill(args, np, torch, pkv):
+    """Chunked prefill: append each sequence's 512-token chunk, then attend it causally
+    over the whole context (one library call each), on the matrix cores (bf16)."""
+    from workloads import chunked_prefill_case
+    print(f"[bench] building inputs: chunked_prefill seed {args.seed}", file=sys.stderr,
+          flush=True)
+    pc = chunked_prefill_case(args.seed)
+    case = pc.case
+    B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            x = x.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    kc, vc = to_dev(case.k_pool[0]), to_dev(case.v_pool[0])
+    tables, ctx = to_dev(case.block_tables), to_dev(case.context_lens)
+    q, k_new, v_new = to_dev(pc.q), to_dev(pc.k_new), to_dev(pc.v_new)
+    cu, start = to_dev(pc.cu_q), to_dev(pc.start_pos)
+    T = int(pc.cu_q[-1])
+    max_q = int(np.diff(pc.cu_q).max())
+    out = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    scale = float(case.scale)
+
+    def prefill():
+        pkv.paged_prefill(q, kc, vc, tables, cu, ctx, max_q, scale=scale, out=out, lse=lse)
+
+    def step():
+        pkv.kv_append(kc, vc, k_new, v_new, tables, start, cu)
+        prefill()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
+    stream = torch.cuda.current_stream()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for _ in range(args.steps):
+        step()
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    step_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+    s_ev.record(stream)
+    for _ in range(args.kernel_reps):
+        prefill()
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    kern_s = s_ev.elapsed_time(e_ev) / 1e3 / args.kernel_reps
+    # causal work: query i of a chunk of L at context n attends n - L + i + 1 keys; per key
+    # and query head 2 D flops for the score and 2 D for the weighted sum
+    keys = 0
+    for s in range(B):
+        n, L = int(case.context_lens[s]), int(pc.cu_q[s + 1] - pc.cu_q[s])
+        keys += L * (n - L) + L * (L + 1) // 2
+    flops = keys * hq * d * 4
+    kv_bytes = int(case.context_lens.sum()) * 2 * hkv * d * case.elem_bytes
+    io_bytes = T * hq * d * (case.elem_bytes + 4) + T * hq * 4
+    tflops = flops / kern_s / 1e12
+    return {
+        "metric": "paged chunked-prefill attention TFLOP/s at 1 GPU",
+        "value": round(flops / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunked_prefill", "seed": args.seed, "batch": B,
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "block_size": 16,
+                   "chunk_tokens": max_q, "sum_context_tokens": int(case.context_lens.sum()),
+                   "query_tokens": T,
+                   "step": "kv_append of the chunks + paged prefill (one launch each)"},
+        "query_tokens_per_s": round(T / step_s, 1),
+        "flops_per_step": flops,
+        "roofline": {
+            "kernel": "prefill_mfma_kernel",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(kern_s * 1e6, 2),
+            "kv_bytes_per_launch": kv_bytes + io_bytes,
+            "kv_gbps_if_read_once": round((kv_bytes + io_bytes) / kern_s / 1e9, 1),
+        },
+        "cpu_baseline": None,
+    }
 
 
 def run_replay(args, np, torch, pkv):
@@ -269,6 +371,9 @@ def main():
 
     if args.workload == "gpt2_replay":
         print(json.dumps(run_replay(args, np, torch, pkv)), flush=True)
+        return
+    if args.workload == "chunked_prefill":
+        print(json.dumps(run_prefill(args, np, torch, pkv)), flush=True)
         return
 
     print(f"[bench] building inputs: {args.workload} seed {args.seed}", file=sys.stderr, flush=True)

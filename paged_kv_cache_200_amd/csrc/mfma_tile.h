@@ -70,6 +70,112 @@ __device__ __forceinline__ void mfma_load_block(MfmaBlock<D>& b, const uint16_t*
   }
 }
 
+// Softmax state of one wave's 16 score rows: lane (c, h) holds row c's running max
+// (log2 units, lazy as in the first pass) and its share of the row's exp-sum, and the
+// unnormalised output of rows 4h .. 4h + 3 at dims c * D/16 + j (tile j).
+template <int D>
+struct MfmaRows {
+  float m_c;
+  float l_part;
+  f32x4_t o[MfmaGeom<D>::kTiles];
+};
+
+template <int D>
+__device__ __forceinline__ void mfma_rows_init(MfmaRows<D>& r) {
+  r.m_c = -INFINITY;
+  r.l_part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < MfmaGeom<D>::kTiles; ++j) r.o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// One 16-token block (token t_base .. t_base + 15) for the wave's 16 rows: row c attends
+// the block's tokens below n_c (its own limit); V of tokens at or past n_max (every row's
+// end) is zeroed first, since a zero weight times a stale NaN would spoil the rows.
+template <int D>
+__device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cur,
+                                                const u32x4_t (&qr)[MfmaGeom<D>::kQkSteps],
+                                                int t_base, int n_c, int n_max, int h,
+                                                float scale_log2) {
+  using Mg = MfmaGeom<D>;
+  f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < Mg::kQkSteps; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
+                                                 __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
+                                                 0);
+  // Scores of row c for tokens 4h + i, masked by the row's own length (select, so
+  // stale or NaN slots never pass).
+  float x[4];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
+    bm = fmaxf(bm, x[i]);
+  }
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const bool raise = bm > r.m_c + kLazyMaxSlack;
+  if (__any(raise)) {
+    float a = 1.0f;
+    if (raise) {
+      a = r.m_c == -INFINITY ? 0.0f : fast_exp2(r.m_c - bm);
+      r.m_c = bm;
+    }
+    r.l_part *= a;
+    // Output rows 4h + i take the factor of the lanes that own score row 4h + i.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(a, 4 * h + i);
+#pragma unroll
+      for (int j = 0; j < Mg::kTiles; ++j) r.o[j][i] *= ai;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - r.m_c);
+    r.l_part += p[i];
+  }
+  // P V on the bf16 MFMA with P split into two bf16 terms, hi = P truncated and
+  // lo = (P - hi) truncated (P - hi is exact in fp32), so the product sees P to about
+  // 2^-16 relative.  A operand: P[row c][tokens 4h .. 4h + 3], the lane's own scores.
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hb[i] = __float_as_uint(p[i]) & 0xffff0000u;
+    lb[i] = __float_as_uint(p[i] - __uint_as_float(hb[i])) & 0xffff0000u;
+  }
+  const i16x4_t a_hi = __builtin_bit_cast(
+      i16x4_t, u32x2_t{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3]});
+  const i16x4_t a_lo = __builtin_bit_cast(
+      i16x4_t, u32x2_t{(lb[0] >> 16) | lb[1], (lb[2] >> 16) | lb[3]});
+  // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
+  if (t_base + kBlockTokens > n_max) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool vok = t_base + 4 * h + i < n_max;
+#pragma unroll
+      for (int w = 0; w < Mg::kVWords; ++w) cur.v[i][w] = vok ? cur.v[i][w] : 0u;
+    }
+  }
+  const auto& v = cur.v;
+  // B operand of tile j: V[tokens 4h .. 4h + 3][dim c * D/16 + j], the even tiles from
+  // the low halves of the lane's words, the odd ones from the high halves.
+#pragma unroll
+  for (int w = 0; w < Mg::kVWords; ++w) {
+    const i16x4_t b_even = __builtin_bit_cast(
+        i16x4_t, u32x2_t{(v[0][w] & 0xffffu) | (v[1][w] << 16),
+                         (v[2][w] & 0xffffu) | (v[3][w] << 16)});
+    const i16x4_t b_odd = __builtin_bit_cast(
+        i16x4_t, u32x2_t{(v[0][w] >> 16) | (v[1][w] & 0xffff0000u),
+                         (v[2][w] >> 16) | (v[3][w] & 0xffff0000u)});
+    r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_even, r.o[2 * w], 0, 0, 0);
+    r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_even, r.o[2 * w], 0, 0, 0);
+    r.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_odd, r.o[2 * w + 1], 0, 0, 0);
+    r.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_odd, r.o[2 * w + 1], 0, 0, 0);
+  }
+}
+
 // LDS of one row tile: per wave the members found not to share the leader's blocks, and
 // per wave and row the softmax state and the unnormalised output.
 template <int D>
@@ -133,11 +239,8 @@ __device__ __forceinline__ unsigned mfma_tile(
     for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
   }
 
-  float m_c = -INFINITY;  // running max of row c, log2 units (lazy, as in the first pass)
-  float l_part = 0.0f;    // this lane's share of row c's exp-sum
-  f32x4_t o[Mg::kTiles];
-#pragma unroll
-  for (int j = 0; j < Mg::kTiles; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  MfmaRows<D> rows;
+  mfma_rows_init<D>(rows);
 
   const int nblk = n_max > tok0 ? (n_max - tok0 + kBlockTokens - 1) / kBlockTokens : 0;
   const int nw = nblk > wave ? (nblk - wave + kTileWaves - 1) / kTileWaves : 0;
@@ -174,83 +277,7 @@ __device__ __forceinline__ unsigned mfma_tile(
   };
   auto process = [&](MfmaBlock<D>& cur, int k) {
     const int t_base = (b0 + wave + kTileWaves * k) * kBlockTokens;  // token of slot 0
-    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < Mg::kQkSteps; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
-                                                   __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
-                                                   0);
-    // Scores of row c for tokens 4h + i, masked by the row's own length (select, so
-    // stale or NaN slots never pass).
-    float x[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, x[i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const bool raise = bm > m_c + kLazyMaxSlack;
-    if (__any(raise)) {
-      float a = 1.0f;
-      if (raise) {
-        a = m_c == -INFINITY ? 0.0f : fast_exp2(m_c - bm);
-        m_c = bm;
-      }
-      l_part *= a;
-      // Output rows 4h + i take the factor of the lanes that own score row 4h + i.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(a, 4 * h + i);
-#pragma unroll
-        for (int j = 0; j < Mg::kTiles; ++j) o[j][i] *= ai;
-      }
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - m_c);
-      l_part += p[i];
-    }
-    // P V on the bf16 MFMA with P split into two bf16 terms, hi = P truncated and
-    // lo = (P - hi) truncated (P - hi is exact in fp32), so the product sees P to about
-    // 2^-16 relative.  A operand: P[row c][tokens 4h .. 4h + 3], the lane's own scores.
-    uint32_t hb[4], lb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hb[i] = __float_as_uint(p[i]) & 0xffff0000u;
-      lb[i] = __float_as_uint(p[i] - __uint_as_float(hb[i])) & 0xffff0000u;
-    }
-    const i16x4_t a_hi = __builtin_bit_cast(
-        i16x4_t, u32x2_t{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3]});
-    const i16x4_t a_lo = __builtin_bit_cast(
-        i16x4_t, u32x2_t{(lb[0] >> 16) | lb[1], (lb[2] >> 16) | lb[3]});
-    // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
-    if (t_base + kBlockTokens > n_max) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool vok = t_base + 4 * h + i < n_max;
-#pragma unroll
-        for (int w = 0; w < Mg::kVWords; ++w) cur.v[i][w] = vok ? cur.v[i][w] : 0u;
-      }
-    }
-    const auto& v = cur.v;
-    // B operand of tile j: V[tokens 4h .. 4h + 3][dim c * D/16 + j], the even tiles from
-    // the low halves of the lane's words, the odd ones from the high halves.
-#pragma unroll
-    for (int w = 0; w < Mg::kVWords; ++w) {
-      const i16x4_t b_even = __builtin_bit_cast(
-          i16x4_t, u32x2_t{(v[0][w] & 0xffffu) | (v[1][w] << 16),
-                           (v[2][w] & 0xffffu) | (v[3][w] << 16)});
-      const i16x4_t b_odd = __builtin_bit_cast(
-          i16x4_t, u32x2_t{(v[0][w] >> 16) | (v[1][w] & 0xffff0000u),
-                           (v[2][w] >> 16) | (v[3][w] & 0xffff0000u)});
-      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_even, o[2 * w], 0, 0, 0);
-      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_even, o[2 * w], 0, 0, 0);
-      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_odd, o[2 * w + 1], 0, 0, 0);
-      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_odd, o[2 * w + 1], 0, 0, 0);
-    }
+    mfma_rows_block<D>(rows, cur, qr, t_base, n_c, n_max, h, scale_log2);
   };
   // Two blocks in flight: the next block's loads are issued before this one's math.
   MfmaBlock<D> bufa, bufb;
@@ -263,9 +290,11 @@ __device__ __forceinline__ unsigned mfma_tile(
       process(bufb, k + 1);
     }
   }
-  float l_c = l_part;
+  float l_c = rows.l_part;
   l_c += __shfl_xor(l_c, 16);
   l_c += __shfl_xor(l_c, 32);
+  const float m_c = rows.m_c;
+  const auto& o = rows.o;
 
   // Merge the waves: each publishes (m, l) per row and its unnormalised rows.
   constexpr int kQuads = Mg::kTiles / 4;  // float4s per lane and row

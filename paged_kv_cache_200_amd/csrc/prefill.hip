@@ -55,23 +55,33 @@ __device__ __forceinline__ Chunk chunk_of(const int32_t* __restrict__ cu_q,
   return c;
 }
 
-// Tiles are taken from the chunk's end (the longest causal ranges) first.
+// Work item w = (tile x, sequence, KV head), x fastest.  The hardware hands workgroups
+// to the eight XCDs round-robin by id, so workgroup b takes item (b % 8) * per + b / 8:
+// the tiles of one (sequence, KV head), which read the same blocks, run on one XCD and
+// share its L2.  Tiles are taken from the chunk's end (the longest causal ranges) first.
+constexpr int kXcds = 8;
+
 template <int D, int G>
 __global__ __launch_bounds__(kTileWaves * kWave) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens, int total_q,
-    int max_q_len, int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2,
-    float* __restrict__ out, float* __restrict__ lse) {
+    int max_q_len, int tiles_x, int batch, int num_q_heads, int num_kv_heads, int num_blocks,
+    float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int kMembers = kMfmaRows / G;  // query tokens per tile
   __shared__ MfmaShared<D> sm;
-  const int s = blockIdx.y;
-  const int kvh = blockIdx.z;
-  const bool first = blockIdx.x == 0 && kvh == 0 && threadIdx.x == 0;
+  const int items = tiles_x * batch * num_kv_heads;
+  const int per = gridDim.x / kXcds;
+  const int w = static_cast<int>(blockIdx.x % kXcds) * per + static_cast<int>(blockIdx.x / kXcds);
+  if (w >= items) return;
+  const int x = w % tiles_x;
+  const int s = (w / tiles_x) % batch;
+  const int kvh = w / (tiles_x * batch);
+  const bool first = x == 0 && kvh == 0 && threadIdx.x == 0;
   const Chunk c = chunk_of(cu_q, ctx_lens, s, total_q, max_q_len, W * kBlockTokens, first);
   const int tiles = (c.len + kMembers - 1) / kMembers;
-  if (static_cast<int>(blockIdx.x) >= tiles) return;
-  const int t0 = (tiles - 1 - static_cast<int>(blockIdx.x)) * kMembers;
+  if (x >= tiles) return;
+  const int t0 = (tiles - 1 - x) * kMembers;
   int lim[kMembers];
   unsigned take = 0;
 #pragma unroll
@@ -151,11 +161,14 @@ template <typename T, int D, int G>
 void prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
     constexpr int kMembers = kMfmaRows / G;
-    const dim3 grid((a.max_q_len + kMembers - 1) / kMembers, a.batch, a.hkv);
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), grid, dim3(kTileWaves * kWave), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
-                       static_cast<const uint16_t*>(a.vc), a.tables, a.W, a.cu_q, a.ctx,
-                       a.total_q, a.max_q_len, a.hq, a.hkv, a.nb, a.scale_log2, a.out, a.lse);
+    const int tiles_x = (a.max_q_len + kMembers - 1) / kMembers;
+    const long long items = static_cast<long long>(tiles_x) * a.batch * a.hkv;
+    const long long per = (items + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(static_cast<unsigned>(per * kXcds)),
+                       dim3(kTileWaves * kWave), 0, stream, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc),
+                       a.tables, a.W, a.cu_q, a.ctx, a.total_q, a.max_q_len, tiles_x, a.batch,
+                       a.hq, a.hkv, a.nb, a.scale_log2, a.out, a.lse);
   } else {
     const dim3 grid((a.max_q_len + kPrefillWaves - 1) / kPrefillWaves, a.batch, a.hkv);
     hipLaunchKernelGGL((prefill_valu_kernel<T, D, G>), grid, dim3(kPrefillWaves * kWave), 0,

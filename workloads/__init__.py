@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     bf16_bits,
     block_refcounts,
     build_case,
+    chunked_prefill_case,
     config_case,
     fork_case,
     fork_groups,

@@ -458,3 +458,35 @@ def allocator_replay_requests(seed: int = 0, n: int = 64):
     prompts = rng.integers(16, 129, size=n).astype(np.int32)
     gens = _lognormal_lengths(rng, n, 48, 0.75, 192)
     return prompts, gens, dict(max_new_tokens=192, total_slots=8192, block_size=16)
+
+
+# --------------------------------------------------------------------------------------
+# Chunked prefill: 16 sequences each append a 512-token chunk onto a prior context of
+# U{0..3584} tokens and attend it causally (bf16, 32/8 heads, head_dim 128).
+# --------------------------------------------------------------------------------------
+
+@dataclass
+class PrefillCase:
+    case: DecodeCase          # pools and tables for the full contexts (prior + chunk)
+    q: np.ndarray             # [T, Hq, D] query rows of the chunks, bf16 bits
+    k_new: np.ndarray         # [T, Hkv, D] the chunks' K, bf16 bits
+    v_new: np.ndarray
+    cu_q: np.ndarray          # int32 [B + 1]
+    start_pos: np.ndarray     # int32 [B]: each chunk's first position (the prior length)
+
+
+def chunked_prefill_case(seed: int = 0, batch: int = 16, chunk: int = 512,
+                         max_prior: int = 3584, hq: int = 32, hkv: int = 8,
+                         d: int = 128) -> PrefillCase:
+    st = _streams(seed)
+    rng = np.random.default_rng(st["lengths"])
+    prior = rng.integers(0, max_prior + 1, size=batch).astype(np.int32)
+    ctx = (prior + chunk).astype(np.int32)
+    case = build_case("chunked_prefill", ctx, hq, hkv, d, "bf16", seed, streams=st)
+    kids = np.random.SeedSequence(entropy=seed, spawn_key=(77,)).spawn(3)
+    T = batch * chunk
+    q = bf16_bits(parallel_normal(kids[0], (T, hq, d)))
+    k_new = bf16_bits(parallel_normal(kids[1], (T, hkv, d)))
+    v_new = bf16_bits(parallel_normal(kids[2], (T, hkv, d)))
+    cu = (np.arange(batch + 1) * chunk).astype(np.int32)
+    return PrefillCase(case, q, k_new, v_new, cu, prior)
