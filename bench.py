@@ -62,6 +62,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time for the oracle baseline (repeats the whole batch)")
     p.add_argument("--no-copy-probe", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the step as one captured HIP graph instead of launching "
+                        "every library call from Python (measured no faster here)")
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="decode fork workloads with the plain path (each fork re-reads the "
                         "shared prefix) instead of the shared-prefix path")
@@ -464,9 +467,24 @@ def main():
               flush=True)
         del src, dst
 
+    run = step
+    if args.graph:
+        # the whole step (every layer's launches) as one HIP graph: same kernels and
+        # inputs, no per-call host work between them
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
+        run()
     torch.cuda.synchronize()
     flags = pkv.device_error()
     if flags:
@@ -478,7 +496,7 @@ def main():
     t0 = time.perf_counter()
     evs[0].record(stream)
     for i in range(args.steps):
-        step()
+        run()
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -578,6 +596,7 @@ def main():
                      "append 1 token/seq + work plan (one launch), split-KV first pass, "
                      "LSE combine"),
             "appended_tokens_per_layer": total_new,
+            "launch": "hip graph of the whole step" if args.graph else "eager",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_ctx / step_s, 1),
