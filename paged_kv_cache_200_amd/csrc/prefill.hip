@@ -6,10 +6,10 @@
 // included): query i sits at position n - q_len + i and attends to tokens [0, that
 // position], through the block table, with explicit lengths.
 //
-// bf16 caches: the matrix-core tile.  A workgroup takes 16 / G consecutive query tokens
-// of one sequence for one KV head, i.e. 16 (token, query head) rows that read the same
-// blocks; each row carries its own causal limit, so one pass over the blocks serves all
-// of them.  fp32 caches: the VALU routine of the decode, one wave per query token.
+// bf16 caches: matrix-core row tiles of 16 (token, query head) rows of one sequence for
+// one KV head, each row with its own causal limit; a workgroup's four waves take
+// consecutive tiles and share every K/V block through LDS.  fp32 caches: the VALU
+// routine of the decode, one wave per query token.
 
 #include "common.h"
 
@@ -55,44 +55,229 @@ __device__ __forceinline__ Chunk chunk_of(const int32_t* __restrict__ cu_q,
   return c;
 }
 
-// Work item w = (tile x, sequence, KV head), x fastest.  The hardware hands workgroups
-// to the eight XCDs round-robin by id, so workgroup b takes item (b % 8) * per + b / 8:
-// the tiles of one (sequence, KV head), which read the same blocks, run on one XCD and
-// share its L2.  Tiles are taken from the chunk's end (the longest causal ranges) first.
-constexpr int kXcds = 8;
+// bf16, LDS-staged: a workgroup of four waves takes kR row tiles per wave, i.e.
+// 4 * kR * (16 / G) consecutive query tokens of one sequence for one KV head.  Each block
+// of the causal range is loaded once per workgroup (every thread fetches 16 bytes of K
+// and of V, so the loads in flight cost few registers), stored to LDS with rows padded by
+// 16 bytes (both operand reads and the stores then touch distinct banks), and read by
+// every wave for all its row tiles: one block load serves 64 * kR rows.  Three LDS stages
+// and three register sets: a block's loads are issued two blocks before it is stored, the
+// next block is stored while the current one is read, one barrier per block.
+constexpr int kLdsWaves = 4;
+constexpr int kLdsThreads = kLdsWaves * kWave;
 
-template <int D, int G>
-__global__ __launch_bounds__(kTileWaves * kWave) void prefill_mfma_kernel(
+template <int D>
+struct LdsStage {
+  static constexpr int kRowElems = D + 8;  // 16-byte pad per token row
+  alignas(16) uint16_t k[kBlockTokens * kRowElems];
+  alignas(16) uint16_t v[kBlockTokens * kRowElems];
+};
+
+template <int D>
+struct StageRegs {
+  static constexpr int kChunks = 2 * kBlockTokens * D / 8;  // 16-byte chunks of K and V
+  static constexpr int kPerThread = (kChunks + kLdsThreads - 1) / kLdsThreads;
+  u32x4_t w[kPerThread];
+};
+
+// Chunk i of a block: i < 2D covers K (token i / (D/8), dims 8 * (i % (D/8)) ..), the rest V.
+template <int D>
+__device__ __forceinline__ void stage_load(StageRegs<D>& r, const uint16_t* __restrict__ kt,
+                                           const uint16_t* __restrict__ vt, int tid) {
+  constexpr int kHalf = StageRegs<D>::kChunks / 2;
+#pragma unroll
+  for (int j = 0; j < StageRegs<D>::kPerThread; ++j) {
+    const int i = tid + j * kLdsThreads;
+    const uint16_t* src = i < kHalf ? kt + i * 8 : vt + (i - kHalf) * 8;
+    r.w[j] = *reinterpret_cast<const u32x4_t*>(src);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_store(LdsStage<D>& st, const StageRegs<D>& r, int tid) {
+  constexpr int kHalf = StageRegs<D>::kChunks / 2;
+  constexpr int kRowChunks = D / 8;
+#pragma unroll
+  for (int j = 0; j < StageRegs<D>::kPerThread; ++j) {
+    const int i = tid + j * kLdsThreads;
+    const int ii = i < kHalf ? i : i - kHalf;
+    uint16_t* dst = (i < kHalf ? st.k : st.v) +
+                    (ii / kRowChunks) * LdsStage<D>::kRowElems + (ii % kRowChunks) * 8;
+    *reinterpret_cast<u32x4_t*>(dst) = r.w[j];
+  }
+}
+
+// The lane's MFMA operands of a staged block (same layouts as mfma_load_block).
+template <int D>
+__device__ __forceinline__ void stage_read(MfmaBlock<D>& b, const LdsStage<D>& st, int c, int h) {
+  using Mg = MfmaGeom<D>;
+  constexpr int RS = LdsStage<D>::kRowElems;
+#pragma unroll
+  for (int k = 0; k < Mg::kQkSteps; ++k)
+    b.k[k] = *reinterpret_cast<const u32x4_t*>(st.k + c * RS + 32 * k + 8 * h);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint16_t* src = st.v + (4 * h + k) * RS + c * Mg::kTiles;
+    if constexpr (Mg::kVWords == 4) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.v[k][j] = w[j];
+    } else {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
+      b.v[k][0] = w[0];
+      b.v[k][1] = w[1];
+    }
+  }
+}
+
+template <int D, int G, int kR>
+__global__ __launch_bounds__(kLdsThreads) void prefill_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens, int total_q,
-    int max_q_len, int tiles_x, int batch, int num_q_heads, int num_kv_heads, int num_blocks,
-    float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kMembers = kMfmaRows / G;  // query tokens per tile
-  __shared__ MfmaShared<D> sm;
-  const int items = tiles_x * batch * num_kv_heads;
-  const int per = gridDim.x / kXcds;
-  const int w = static_cast<int>(blockIdx.x % kXcds) * per + static_cast<int>(blockIdx.x / kXcds);
-  if (w >= items) return;
-  const int x = w % tiles_x;
-  const int s = (w / tiles_x) % batch;
-  const int kvh = w / (tiles_x * batch);
-  const bool first = x == 0 && kvh == 0 && threadIdx.x == 0;
-  const Chunk c = chunk_of(cu_q, ctx_lens, s, total_q, max_q_len, W * kBlockTokens, first);
-  const int tiles = (c.len + kMembers - 1) / kMembers;
-  if (x >= tiles) return;
-  const int t0 = (tiles - 1 - x) * kMembers;
-  int lim[kMembers];
-  unsigned take = 0;
+    int max_q_len, int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2,
+    float* __restrict__ out, float* __restrict__ lse) {
+  using Mg = MfmaGeom<D>;
+  constexpr int kMembers = kMfmaRows / G;  // query tokens per row tile
+  constexpr int kRows = kMembers * G;
+  constexpr int kGroupTokens = kMembers * kR * kLdsWaves;
+  __shared__ LdsStage<D> stage[3];
+  __shared__ int s_ids[kWave];
+  const int s = blockIdx.y;
+  const int kvh = blockIdx.z;
+  const int tid = threadIdx.x;
+  const bool first = blockIdx.x == 0 && kvh == 0 && tid == 0;
+  const Chunk ch = chunk_of(cu_q, ctx_lens, s, total_q, max_q_len, W * kBlockTokens, first);
+  const int groups = (ch.len + kGroupTokens - 1) / kGroupTokens;
+  if (static_cast<int>(blockIdx.x) >= groups) return;  // whole workgroup: uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int c = lane % 16;
+  const int h = lane / 16;
+  const int tg = (groups - 1 - static_cast<int>(blockIdx.x)) * kGroupTokens;  // group's first
+  const int pos_g = ch.n - ch.len + tg;
+  // The group's causal range ends at its last live token.
+  const int g_members = min(kGroupTokens, ch.len - tg);
+  const int n_group = pos_g + g_members;
+  const int nblk = (n_group + kBlockTokens - 1) / kBlockTokens;
+
+  // This wave's row tiles: tokens tg + (wave * kR + r) * kMembers + c / G.
+  int n_c[kR], members[kR], tile_end[kR];
+  int n_wave = 0;
+  u32x4_t qr[kR][Mg::kQkSteps];
+  MfmaRows<D> rows[kR];
 #pragma unroll
-  for (int mi = 0; mi < kMembers; ++mi) {
-    const int t = t0 + mi;
-    lim[mi] = t < c.len ? c.n - c.len + t + 1 : 0;
-    if (t < c.len) take |= 1u << mi;
+  for (int r = 0; r < kR; ++r) {
+    const int t0 = tg + (wave * kR + r) * kMembers;
+    members[r] = max(0, min(kMembers, ch.len - t0));
+    const int pos0 = ch.n - ch.len + t0;
+    const bool live = c < kRows && c / G < members[r];
+    n_c[r] = live ? pos0 + c / G + 1 : 0;
+    tile_end[r] = members[r] > 0 ? pos0 + members[r] : 0;
+    n_wave = max(n_wave, tile_end[r]);
+#pragma unroll
+    for (int k = 0; k < Mg::kQkSteps; ++k) qr[r][k] = u32x4_t{0u, 0u, 0u, 0u};
+    if (live) {
+      const uint16_t* qrow = q + (static_cast<size_t>(ch.r0 + t0 + c / G) * num_q_heads +
+                                  kvh * G + c % G) * D + 8 * h;
+#pragma unroll
+      for (int k = 0; k < Mg::kQkSteps; ++k)
+        qr[r][k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
+    }
+    mfma_rows_init<D>(rows[r]);
   }
-  mfma_tile<D, G>(sm, q, kc, vc, tables + static_cast<size_t>(s) * W, nullptr, W, lim, take,
-                  c.r0 + t0, kvh, num_q_heads, num_kv_heads, num_blocks, scale_log2, 0, 0, 1,
-                  out, lse);
+
+  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
+  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
+  const int32_t* trow = tables + static_cast<size_t>(s) * W;
+  // Block ids, 64 at a time: wave 0 fetches them into LDS; the barrier that publishes a
+  // staged block also publishes the ids of the blocks after it.
+  auto block_ptr = [&](int id, const uint16_t* base) {
+    return base + static_cast<size_t>(id) * block_elems + kvh * head_elems;
+  };
+  auto fetch_ids = [&](int from) {
+    if (wave == 0) {
+      const int k = from + lane;
+      int id = k < nblk ? trow[k] : 0;
+      const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
+      if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+      s_ids[lane] = bad ? 0 : id;
+    }
+  };
+  auto compute = [&](const LdsStage<D>& st, int b) {
+    const int t_base = b * kBlockTokens;
+    if (t_base >= n_wave) return;  // past every row of this wave (causal): nothing to add
+    MfmaBlock<D> cur;
+    stage_read<D>(cur, st, c, h);
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+      if (t_base < tile_end[r])
+        mfma_rows_block<D>(rows[r], cur, qr[r], t_base, n_c[r], n_wave, h, scale_log2);
+  };
+
+  // Three LDS stages, three register sets: the loads of block j are issued two blocks
+  // before it is stored to LDS (block j lives in stage j % 3).
+  auto issue = [&](int j, StageRegs<D>& r) {
+    if (j % kWave == 0 && j > 0) {
+      __syncthreads();  // every thread has read the previous ids
+      fetch_ids(j);
+      __syncthreads();
+    }
+    const int id = s_ids[j % kWave];
+    stage_load<D>(r, block_ptr(id, kc), block_ptr(id, vc), tid);
+  };
+  StageRegs<D> r0, r1, r2;
+  fetch_ids(0);
+  __syncthreads();
+  if (nblk > 0) issue(0, r0);
+  if (nblk > 1) issue(1, r1);
+  if (nblk > 2) issue(2, r2);
+  if (nblk > 0) stage_store<D>(stage[0], r0, tid);
+  __syncthreads();
+  for (int b = 0; b < nblk; b += 3) {
+    // stage[0] holds block b; r1, r2 hold blocks b + 1, b + 2 in flight
+    if (b + 3 < nblk) issue(b + 3, r0);
+    compute(stage[0], b);
+    if (b + 1 < nblk) stage_store<D>(stage[1], r1, tid);
+    __syncthreads();
+    if (b + 1 >= nblk) break;
+    if (b + 4 < nblk) issue(b + 4, r1);
+    compute(stage[1], b + 1);
+    if (b + 2 < nblk) stage_store<D>(stage[2], r2, tid);
+    __syncthreads();
+    if (b + 2 >= nblk) break;
+    if (b + 5 < nblk) issue(b + 5, r2);
+    compute(stage[2], b + 2);
+    if (b + 3 < nblk) stage_store<D>(stage[0], r0, tid);
+    __syncthreads();
+  }
+
+  // Row c's totals live on the four lanes with lane % 16 == c; output row 4h + i's on
+  // lane (c, h).  Each output row takes its max and sum from a lane owning its score row.
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    float l_c = rows[r].l_part;
+    l_c += __shfl_xor(l_c, 16);
+    l_c += __shfl_xor(l_c, 32);
+    const int t0 = tg + (wave * kR + r) * kMembers;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * h + i;
+      const float L = __shfl(l_c, rr);
+      const float M = __shfl(rows[r].m_c, rr);
+      if (rr >= kRows || rr / G >= members[r]) continue;
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const size_t sh =
+          static_cast<size_t>(ch.r0 + t0 + rr / G) * num_q_heads + kvh * G + rr % G;
+      float* dst = out + sh * D + c * Mg::kTiles;
+#pragma unroll
+      for (int u = 0; u < Mg::kTiles / 4; ++u)
+        *reinterpret_cast<float4*>(dst + 4 * u) =
+            make_float4(rows[r].o[4 * u][i] * inv, rows[r].o[4 * u + 1][i] * inv,
+                        rows[r].o[4 * u + 2][i] * inv, rows[r].o[4 * u + 3][i] * inv);
+      if (c == 0 && lse != nullptr) lse[sh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
 }
 
 constexpr int kPrefillWaves = 4;
@@ -160,15 +345,13 @@ struct PrefillArgs {
 template <typename T, int D, int G>
 void prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    constexpr int kMembers = kMfmaRows / G;
-    const int tiles_x = (a.max_q_len + kMembers - 1) / kMembers;
-    const long long items = static_cast<long long>(tiles_x) * a.batch * a.hkv;
-    const long long per = (items + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(static_cast<unsigned>(per * kXcds)),
-                       dim3(kTileWaves * kWave), 0, stream, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc),
-                       a.tables, a.W, a.cu_q, a.ctx, a.total_q, a.max_q_len, tiles_x, a.batch,
-                       a.hq, a.hkv, a.nb, a.scale_log2, a.out, a.lse);
+    constexpr int kR = 1;
+    constexpr int kGroupTokens = kMfmaRows / G * kR * kLdsWaves;
+    const dim3 grid((a.max_q_len + kGroupTokens - 1) / kGroupTokens, a.batch, a.hkv);
+    hipLaunchKernelGGL((prefill_lds_kernel<D, G, kR>), grid, dim3(kLdsThreads), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
+                       static_cast<const uint16_t*>(a.vc), a.tables, a.W, a.cu_q, a.ctx,
+                       a.total_q, a.max_q_len, a.hq, a.hkv, a.nb, a.scale_log2, a.out, a.lse);
   } else {
     const dim3 grid((a.max_q_len + kPrefillWaves - 1) / kPrefillWaves, a.batch, a.hkv);
     hipLaunchKernelGGL((prefill_valu_kernel<T, D, G>), grid, dim3(kPrefillWaves * kWave), 0,
