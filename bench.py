@@ -35,7 +35,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_high_concurrency.json")
 # the sources of the first pass's translation unit; counters taken on other sources are
 # not reported
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
-               for f in ("paged_decode.hip", "common.h", "append_row.h", "mfma_tile.h")]
+               for f in ("paged_decode.hip", "common.h", "append_row.h", "mfma_tile.h",
+                         "valu_attend.h")]
 
 
 def decode_source_digest():
