@@ -371,7 +371,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import paged_kv_cache_200_amd as pkv
-    from workloads import bf16_bits, block_refcounts, config_case, fork_groups, parallel_normal
+    from workloads import config_case, decode_step_inputs, fork_groups
 
     if args.workload == "gpt2_replay":
         print(json.dumps(run_replay(args, np, torch, pkv)), flush=True)
@@ -404,27 +404,12 @@ def main():
     tables = to_dev(case.block_tables)
     ctx = to_dev(case.context_lens)
     max_ctx = int(case.context_lens.max())
-    # the token appended this step sits at position ctx - 1 (it attends to itself)
-    ss = np.random.SeedSequence(entropy=args.seed, spawn_key=(99,))
-    kn = parallel_normal(ss.spawn(1)[0], (B, hkv, d))
-    vn = parallel_normal(ss.spawn(1)[0], (B, hkv, d))
-    if case.kv_dtype == "bf16":
-        kn, vn = bf16_bits(kn), bf16_bits(vn)
-    k_new, v_new = to_dev(kn), to_dev(vn)
-    start_np = (case.context_lens - 1).clip(min=0).astype(np.int32)
-    counts = (case.context_lens > 0).astype(np.int32)
-    if case.shared_blocks:
-        # copy-on-write: a token is never written into a block that several sequences
-        # hold (a fork with no private token would first get its own copy)
-        refs = block_refcounts(case)
-        for s_ in range(B):
-            if counts[s_] and refs[int(case.block_tables[s_, start_np[s_] // 16])] > 1:
-                counts[s_] = 0
-    start = to_dev(start_np)
-    cu = to_dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
-    total_new = int(counts.sum())
-    kn, vn = kn[counts > 0], vn[counts > 0]
-    k_new, v_new = to_dev(kn), to_dev(vn)
+    # the token appended this step sits at position ctx - 1 (it attends to itself); fork
+    # members without a private block append nothing (copy-on-write)
+    si = decode_step_inputs(case, args.seed)
+    start, cu = to_dev(si.start_pos), to_dev(si.cu_new)
+    total_new = int(si.cu_new[-1])
+    k_new, v_new = to_dev(si.k_new), to_dev(si.v_new)
     out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
     if shared_path:

@@ -17,6 +17,7 @@ from .synth import (  # noqa: F401
     build_case,
     chunked_prefill_case,
     config_case,
+    decode_step_inputs,
     fork_case,
     fork_groups,
     parallel_normal,

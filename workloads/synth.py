@@ -491,3 +491,36 @@ def chunked_prefill_case(seed: int = 0, batch: int = 16, chunk: int = 512,
     v_new = bf16_bits(parallel_normal(kids[2], (T, hkv, d)))
     cu = (np.arange(batch + 1) * chunk).astype(np.int32)
     return PrefillCase(case, q, k_new, v_new, cu, prior)
+
+
+# --------------------------------------------------------------------------------------
+# The decode step's new tokens: one per sequence at position ctx - 1 (the context counts
+# the token appended this step).  Copy-on-write: a token is never written into a block
+# that several sequences hold (a fork with no private token would first copy it), so such
+# sequences append nothing this step.
+# --------------------------------------------------------------------------------------
+
+@dataclass
+class StepInputs:
+    k_new: np.ndarray      # [T, Hkv, D] cache dtype
+    v_new: np.ndarray
+    start_pos: np.ndarray  # int32 [B]
+    cu_new: np.ndarray     # int32 [B + 1]
+
+
+def decode_step_inputs(case: DecodeCase, seed: int) -> StepInputs:
+    B, hkv, d = case.batch, case.num_kv_heads, case.head_dim
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(99,))
+    kn = parallel_normal(ss.spawn(1)[0], (B, hkv, d))
+    vn = parallel_normal(ss.spawn(1)[0], (B, hkv, d))
+    if case.kv_dtype == "bf16":
+        kn, vn = bf16_bits(kn), bf16_bits(vn)
+    start = (case.context_lens - 1).clip(min=0).astype(np.int32)
+    counts = (case.context_lens > 0).astype(np.int32)
+    if case.shared_blocks:
+        refs = block_refcounts(case)
+        for s in range(B):
+            if counts[s] and refs[int(case.block_tables[s, start[s] // BLOCK_SIZE])] > 1:
+                counts[s] = 0
+    cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return StepInputs(kn[counts > 0], vn[counts > 0], start, cu)
