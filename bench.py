@@ -32,11 +32,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_high_concurrency.json")
-# the sources of the first pass's translation unit; counters taken on other sources are
-# not reported
+# the sources that define the first pass (and the plan/append prologue of its step);
+# counters taken on other sources are not reported
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
-               for f in ("paged_decode.hip", "common.h", "append_row.h", "mfma_tile.h",
-                         "valu_attend.h")]
+               for f in ("paged_decode.hip", "common.h", "append_row.h", "valu_attend.h")]
 
 
 def decode_source_digest():
