@@ -70,6 +70,11 @@ __device__ __forceinline__ void mfma_load_block(MfmaBlock<D>& b, const uint16_t*
   }
 }
 
+// v_perm_b32 selectors for perm(hi_word, lo_word, sel): result byte k is byte sel[k] of
+// the 8-byte value hi_word:lo_word (0-3 lo_word, 4-7 hi_word).
+constexpr uint32_t kLowHalves = 0x05040100u;   // lo16(lo_word) | lo16(hi_word) << 16
+constexpr uint32_t kHighHalves = 0x07060302u;  // hi16(lo_word) | hi16(hi_word) << 16
+
 // Softmax state of one wave's 16 score rows: lane (c, h) holds row c's running max
 // (log2 units, lazy as in the first pass) and its share of the row's exp-sum, and the
 // unnormalised output of rows 4h .. 4h + 3 at dims c * D/16 + j (tile j).
@@ -142,16 +147,20 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
   // P V on the bf16 MFMA with P split into two bf16 terms, hi = P truncated and
   // lo = (P - hi) truncated (P - hi is exact in fp32), so the product sees P to about
   // 2^-16 relative.  A operand: P[row c][tokens 4h .. 4h + 3], the lane's own scores.
-  uint32_t hb[4], lb[4];
+  // (v_perm_b32 byte selects: kHighHalves packs the high 16 bits of two words, low word
+  // first; kLowHalves their low 16 bits.)
+  uint32_t pw[4], rw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    hb[i] = __float_as_uint(p[i]) & 0xffff0000u;
-    lb[i] = __float_as_uint(p[i] - __uint_as_float(hb[i])) & 0xffff0000u;
+    pw[i] = __float_as_uint(p[i]);
+    rw[i] = __float_as_uint(p[i] - __uint_as_float(pw[i] & 0xffff0000u));  // exact remainder
   }
   const i16x4_t a_hi = __builtin_bit_cast(
-      i16x4_t, u32x2_t{(hb[0] >> 16) | hb[1], (hb[2] >> 16) | hb[3]});
+      i16x4_t, u32x2_t{__builtin_amdgcn_perm(pw[1], pw[0], kHighHalves),
+                       __builtin_amdgcn_perm(pw[3], pw[2], kHighHalves)});
   const i16x4_t a_lo = __builtin_bit_cast(
-      i16x4_t, u32x2_t{(lb[0] >> 16) | lb[1], (lb[2] >> 16) | lb[3]});
+      i16x4_t, u32x2_t{__builtin_amdgcn_perm(rw[1], rw[0], kHighHalves),
+                       __builtin_amdgcn_perm(rw[3], rw[2], kHighHalves)});
   // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
   if (t_base + kBlockTokens > n_max) {
 #pragma unroll
@@ -168,11 +177,11 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
 #pragma unroll
   for (int w = 0; w < Mg::kVWords; ++w) {
     const i16x4_t b_even = __builtin_bit_cast(
-        i16x4_t, u32x2_t{(v[0][w] & 0xffffu) | (v[1][w] << 16),
-                         (v[2][w] & 0xffffu) | (v[3][w] << 16)});
+        i16x4_t, u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], kLowHalves),
+                         __builtin_amdgcn_perm(v[3][w], v[2][w], kLowHalves)});
     const i16x4_t b_odd = __builtin_bit_cast(
-        i16x4_t, u32x2_t{(v[0][w] >> 16) | (v[1][w] & 0xffff0000u),
-                         (v[2][w] >> 16) | (v[3][w] & 0xffff0000u)});
+        i16x4_t, u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], kHighHalves),
+                         __builtin_amdgcn_perm(v[3][w], v[2][w], kHighHalves)});
     r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_even, r.o[2 * w], 0, 0, 0);
     r.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_odd, r.o[2 * w + 1], 0, 0, 0);
     r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_even, r.o[2 * w], 0, 0, 0);
