@@ -44,8 +44,6 @@ namespace {
 // lane p holds partition p's log-sum-exp (64 partitions per round), so the max and the
 // weight sum are wave reductions; the weighted sum of the partial outputs then streams
 // the partitions with every lane owning D/64 output dims, four partitions per step.
-// Used by the combine kernel and by the first pass's merging workgroup, so both give
-// bit-identical results.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
@@ -151,11 +149,20 @@ constexpr int kSlotMask = kDirectFlag - 1;
 
 // NW wavefronts per workgroup.  NW > 1: the waves share one (sequence, KV head,
 // partition) and take its blocks round-robin, merging through LDS at the end.  NW == 1:
-// one wave owns the unit and writes its result straight from registers.
-// DEPTH: 16-token blocks whose loads are in flight per wave (1 being processed,
-// DEPTH - 1 prefetched).
-template <typename T, int D, int G, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
+// one wave owns the unit and writes its result straight from registers.  Each wave keeps
+// two 16-token blocks in flight.
+//
+// Workgroups per compute unit the register allocation is held to: two (eight waves, at
+// most 256 registers per lane) where that fits without spilling, measured per shape with
+// the compiler's resource report; the other shapes take what their registers allow.
+template <typename T, int D, int G>
+constexpr int pass1_min_workgroups() {
+  constexpr int max_g = sizeof(T) == 2 ? (D == 64 ? 7 : 4) : (D == 64 ? 5 : 2);
+  return G <= max_g ? 2 : 1;
+}
+
+template <typename T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void decode_pass1_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ tables, int W, const int32_t* __restrict__ ctx_lens,
     int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
@@ -209,9 +216,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_pass1_kernel(
   const int lane = threadIdx.x % kWave;
 
   GroupState<T, D, G> st;
-  attend_range<T, D, G, NW, DEPTH, true>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
-                                         num_kv_heads, num_blocks, scale_log2, tok0, tok1, wave,
-                                         lane);
+  attend_range<T, D, G, NW, true>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
+                                  num_kv_heads, num_blocks, scale_log2, tok0, tok1, wave, lane);
   const int grp = lane / kLanesPerToken;
   const int sub = lane % kLanesPerToken;
 
@@ -459,8 +465,10 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
     }
     const int incl = block_scan_inclusive(s_scan, u.full);
     const int first = s_full_total + incl - u.full;
-    for (int p = 0; p < u.full; ++p)
-      plan[first + p] = make_int4(s, u.base + p * P, u.base + (p + 1) * P, unit_slot(u, p));
+    for (int p = 0; p < u.full; ++p) {
+      const int t0 = u.base + p * P;
+      plan[first + p] = make_int4(s, t0, t0 + P, unit_slot(u, p));
+    }
     __syncthreads();
     if (tid == kPlanThreads - 1) s_full_total += incl;
     __syncthreads();
@@ -476,8 +484,8 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
     const SeqUnits u = s == tid ? first : seq_units(in, s, starts);
     if (u.tail) {
       const int t0 = u.base + u.full * P;
-      plan[atomicAdd(&s_cursor[key_of(u.tail_len)], 1)] =
-          make_int4(s, t0, t0 + u.tail_len, unit_slot(u, u.full));
+      const int i = atomicAdd(&s_cursor[key_of(u.tail_len)], 1);
+      plan[i] = make_int4(s, t0, t0 + u.tail_len, unit_slot(u, u.full));
     }
   }
 }
@@ -533,7 +541,7 @@ __device__ __forceinline__ void shared_member(
   // the block boundary tok0 (attend_range needs a block-aligned start).
   const int t1 = max(tok0, min(tok1, n));
   GroupState<T, D, G> st;
-  attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
+  attend_range<T, D, G, 1, false>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
                                      num_kv_heads, num_blocks, scale_log2, tok0, t1, 0, lane);
   if (grp != 0) return;
 #pragma unroll
@@ -689,7 +697,7 @@ using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const vo
                           float*, float*, float*, float*, const int4*, const int*);
 
 // order = kOrderPlanned: plan/plan_count from plan_kernel, grid of batch * np units.
-template <int NW, int DEPTH, typename T, int D, int G>
+template <int NW, typename T, int D, int G>
 void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t stream,
                   const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                   const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
@@ -702,7 +710,7 @@ void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t st
     grid = dim3(np, num_kv_heads, batch);
   else
     grid = dim3(num_kv_heads, batch, np);
-  hipLaunchKernelGGL((decode_pass1_kernel<T, D, G, NW, DEPTH>), grid, dim3(NW * kWave), 0,
+  hipLaunchKernelGGL((decode_pass1_kernel<T, D, G, NW>), grid, dim3(NW * kWave), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
                      part_tokens, max_parts, part_out, part_lse, out, lse, order, plan,
@@ -717,9 +725,9 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
                    const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                    int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
                    float* lse, const int4* plan, const int* plan_count) {
-  pass1_launch<4, 2, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx,
-                              hq, hkv, nb, scale_log2, part_tokens, max_parts, part_out,
-                              part_lse, out, lse, plan, plan_count);
+  pass1_launch<4, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx, hq,
+                           hkv, nb, scale_log2, part_tokens, max_parts, part_out, part_lse, out,
+                           lse, plan, plan_count);
 }
 
 struct SharedArgs {

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_valu_kernel(
   if (t >= c.len) return;
   const int row = c.r0 + t;
   GroupState<T, D, G> st;
-  attend_range<T, D, G, 1, 2, false>(st, q, kc, vc, tables, W, s, row, kvh, num_q_heads,
+  attend_range<T, D, G, 1, false>(st, q, kc, vc, tables, W, s, row, kvh, num_q_heads,
                                      num_kv_heads, num_blocks, scale_log2, 0,
                                      c.n - c.len + t + 1, 0, lane);
   const int grp = lane / kLanesPerToken;

@@ -44,20 +44,13 @@ __device__ __forceinline__ float dot_word<float>(uint32_t qw, uint32_t kw, float
   return fmaf(__uint_as_float(qw), __uint_as_float(kw), acc);
 }
 
-// Widen the words of one token's chunks to float32 values, in element order.
-template <typename T, int D>
-__device__ __forceinline__ void widen(const uint32_t (&w)[Geom<T, D>::kWords],
-                                      float (&v)[Geom<T, D>::kElems]) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int j = 0; j < Geom<T, D>::kWords; ++j) {
-      v[2 * j] = bf16_lo(w[j]);
-      v[2 * j + 1] = bf16_hi(w[j]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < Geom<T, D>::kWords; ++j) v[j] = __uint_as_float(w[j]);
-  }
+// Element e of a token's words as float32 (e compile-time after unrolling).
+template <typename T, int N>
+__device__ __forceinline__ float elem_of(const uint32_t (&w)[N], int e) {
+  if constexpr (sizeof(T) == 2)
+    return (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+  else
+    return __uint_as_float(w[e]);
 }
 
 template <typename T, int D>
@@ -164,31 +157,35 @@ __device__ __forceinline__ void process_block(const TokenRegs<T, D>& r,
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) st.l[g] += p[0][g] + p[1][g];
-  float v0[Gm::kElems], v1[Gm::kElems];
-  widen<T, D>(r.v[0], v0);
-  widen<T, D>(r.v[1], v1);
-  if constexpr (kMasked) {
-    // select, not multiply: stale or NaN slots must not reach the accumulator
+  // V is widened one element at a time, right before its G uses, which keeps the
+  // widened block out of the register file while the next block's loads are in flight.
 #pragma unroll
-    for (int e = 0; e < Gm::kElems; ++e) {
-      v0[e] = valid[0] ? v0[e] : 0.0f;
-      v1[e] = valid[1] ? v1[e] : 0.0f;
+  for (int e = 0; e < Gm::kElems; ++e) {
+    float x0 = elem_of<T>(r.v[0], e);
+    float x1 = elem_of<T>(r.v[1], e);
+    if constexpr (kMasked) {
+      // select, not multiply: stale or NaN slots must not reach the accumulator
+      x0 = valid[0] ? x0 : 0.0f;
+      x1 = valid[1] ? x1 : 0.0f;
     }
-  }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int e = 0; e < Gm::kElems; ++e)
-      st.acc[g][e] = fmaf(p[1][g], v1[e], fmaf(p[0][g], v0[e], st.acc[g][e]));
+    for (int g = 0; g < G; ++g) st.acc[g][e] = fmaf(p[1][g], x1, fmaf(p[0][g], x0, st.acc[g][e]));
   }
 }
 
 // One wave's share of a unit: attend this KV head's G query rows of q row `qrow` over
 // the tokens [tok0, tok1) of the sequence whose block-table row is `s` (tok0 a multiple
-// of the block size, tok0 <= tok1), taking the range's full blocks wave, wave + NW, ...
-// (and the trailing partial block if it falls to this wave), then merge the wave's 8
-// token groups so that every lane holds the wave's totals (m, l, acc) for its dims.
-template <typename T, int D, int G, int NW, int DEPTH, bool kStreaming>
+// of the block size, tok0 <= tok1), taking the range's blocks wave, wave + NW, ... (the
+// last one partial when it holds the range end), then merge the wave's 8 token groups so
+// that every lane holds the wave's totals (m, l, acc) for its dims.
+//
+// Blocks stream two deep: block k + 1's loads are in flight while block k is processed.
+// Every K/V load of the steady loop is unconditional and shares straight-line code with
+// the processing it overlaps: at a join after a conditional load the compiler's wait
+// counts must hold on both paths, so it would wait for the prefetched block as well.
+// Block ids come 64 at a time, one per lane, and are read from the register with
+// readlane.
+template <typename T, int D, int G, int NW, bool kStreaming>
 __device__ __forceinline__ void attend_range(GroupState<T, D, G>& st, const T* __restrict__ q,
                                              const T* __restrict__ kc, const T* __restrict__ vc,
                                              const int32_t* __restrict__ tables, int W, int s,
@@ -198,6 +195,42 @@ __device__ __forceinline__ void attend_range(GroupState<T, D, G>& st, const T* _
   using Gm = Geom<T, D>;
   const int grp = lane / kLanesPerToken;
   const int sub = lane % kLanesPerToken;
+  const int b_begin = tok0 / kBlockTokens;
+  const int nfull = tok1 / kBlockTokens - b_begin;  // blocks wholly inside [tok0, tok1)
+  const int tail = tok1 % kBlockTokens;             // valid tokens of a trailing partial block
+  const int nb = nfull + (tail != 0 ? 1 : 0);
+  const int n_w = nb > wave ? (nb - wave + NW - 1) / NW : 0;  // this wave's blocks
+  // The partial block (index nfull) is the last block of wave nfull % NW.
+  const int last_valid =
+      (tail != 0 && n_w > 0 && wave + NW * (n_w - 1) == nfull) ? tail : kBlockTokens;
+
+  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
+  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
+  const T* kbase = kc + kvh * head_elems;
+  const T* vbase = vc + kvh * head_elems;
+  const int lane_off = grp * D + sub * Gm::kChunkElems;
+  // The wave's k-th block id is trow[NW * k].
+  const int32_t* trow = tables + static_cast<size_t>(s) * W + b_begin + wave;
+
+  // An id outside the pool reads block 0 instead and is reported once, at the end.
+  bool bad_id = false;
+  auto fetch_ids = [&](int base) {  // lane j: raw id of the wave's block base + j
+    const int k = base + lane;
+    return k < n_w ? trow[NW * k] : 0;
+  };
+  auto load = [&](TokenRegs<T, D>& r, int raw_id) {
+    const bool bad = static_cast<unsigned>(raw_id) >= static_cast<unsigned>(num_blocks);
+    bad_id |= bad;
+    const size_t blk = bad ? 0 : static_cast<size_t>(raw_id);
+    load_block<T, D, kStreaming>(r, kbase + blk * block_elems, vbase + blk * block_elems,
+                                 lane_off);
+  };
+
+  // The first window's ids, then its first block, then the query rows.
+  TokenRegs<T, D> r0, r1;
+  int ids = fetch_ids(0);
+  if (n_w > 0) load(r0, __builtin_amdgcn_readlane(ids, 0));
+
   // Query rows of this KV head's group, this lane's dims, raw bits.
   uint32_t qr[G][Gm::kWords];
 #pragma unroll
@@ -220,71 +253,43 @@ __device__ __forceinline__ void attend_range(GroupState<T, D, G>& st, const T* _
     for (int e = 0; e < Gm::kElems; ++e) st.acc[g][e] = 0.0f;
   }
 
-  const int b_begin = tok0 / kBlockTokens;
-  const int nfull = tok1 / kBlockTokens - b_begin;  // blocks wholly inside [tok0, tok1)
-  const int tail = tok1 % kBlockTokens;             // valid tokens of a trailing partial block
-  const int nfull_w = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
+  auto process = [&](const TokenRegs<T, D>& r) {
+    process_block<T, D, G, false>(r, qr, st, scale_log2, grp, kBlockTokens);
+  };
+  auto process_last = [&](const TokenRegs<T, D>& r, int valid) {
+    if (valid == kBlockTokens)
+      process_block<T, D, G, false>(r, qr, st, scale_log2, grp, kBlockTokens);
+    else
+      process_block<T, D, G, true>(r, qr, st, scale_log2, grp, valid);
+  };
 
-  const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
-  const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
-  const T* kbase = kc + kvh * head_elems;
-  const T* vbase = vc + kvh * head_elems;
-  const int lane_off = grp * D + sub * Gm::kChunkElems;
-  const int32_t* trow = tables + static_cast<size_t>(s) * W;
-
-  // Block ids of this wave's full blocks, 64 at a time, one per lane.
-  int id_base = 0;
-  auto fetch_ids = [&](int base) -> int {
-    const int k = base + lane;
-    int id = 0;
-    bool bad = false;
-    if (k < nfull_w) {
-      id = trow[b_begin + wave + NW * k];
-      bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
-      id = bad ? 0 : id;
+  // Windows of 64 blocks; a window's first block is already loading into r0 when it
+  // starts.
+  for (int wb = 0; wb < n_w; wb += kWave) {
+    const int n = min(kWave, n_w - wb);
+    const int valid = wb + n == n_w ? last_valid : kBlockTokens;
+    auto id = [&](int k) { return __builtin_amdgcn_readlane(ids, k); };
+    int k = 0;  // block k is in r0
+    for (; k + 2 < n; k += 2) {
+      load(r1, id(k + 1));
+      process(r0);  // block k
+      load(r0, id(k + 2));
+      process(r1);  // block k + 1
     }
-    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-    return id;
-  };
-  int ids = fetch_ids(0);
-  auto block_of = [&](int k) -> int {  // called with k = 0, 1, 2, ... in order
-    if (k - id_base >= kWave) {
-      id_base += kWave;
-      ids = fetch_ids(id_base);
-    }
-    return __builtin_amdgcn_readlane(ids, k - id_base);
-  };
-  auto load = [&](TokenRegs<T, D>& r, int blk) {
-    load_block<T, D, kStreaming>(r, kbase + static_cast<size_t>(blk) * block_elems,
-                     vbase + static_cast<size_t>(blk) * block_elems, lane_off);
-  };
-
-  TokenRegs<T, D> rr[DEPTH];
-#pragma unroll
-  for (int j = 0; j + 1 < DEPTH; ++j)
-    if (j < nfull_w) load(rr[j], block_of(j));
-  for (int k = 0; k < nfull_w; k += DEPTH) {
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      if (k + j < nfull_w) {
-        const int ahead = k + j + DEPTH - 1;
-        if (ahead < nfull_w) load(rr[(j + DEPTH - 1) % DEPTH], block_of(ahead));
-        process_block<T, D, G, false>(rr[j], qr, st, scale_log2, grp, kBlockTokens);
+    // One or two blocks of the window remain; block k is in r0.
+    if (n - k == 2) {
+      load(r1, id(k + 1));
+      process(r0);
+      if (wb + kWave < n_w) {  // next window: its ids, then its first block
+        ids = fetch_ids(wb + kWave);
+        load(r0, __builtin_amdgcn_readlane(ids, 0));
       }
+      process_last(r1, valid);
+    } else {  // only in the last window: a full window has an even count
+      process_last(r0, valid);
     }
   }
-
-  // The trailing partial block (only in the partition holding the sequence end)
-  // goes to the wave next in the round-robin.
-  if (tail != 0 && wave == nfull % NW) {
-    int b = trow[b_begin + nfull];
-    if (static_cast<unsigned>(b) >= static_cast<unsigned>(num_blocks)) {
-      if (lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-      b = 0;
-    }
-    load(rr[0], b);
-    process_block<T, D, G, true>(rr[0], qr, st, scale_log2, grp, tail);
-  }
+  if (bad_id && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
 
   // Merge the 8 token groups of the wave (lanes with equal `sub` hold the same dims).
 #pragma unroll
