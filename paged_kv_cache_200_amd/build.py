@@ -37,8 +37,13 @@ def _hipcc() -> str:
 
 
 def _hip_flags():
+    # -amdgpu-mfma-vgpr-form: matrix-core accumulators in ordinary VGPRs rather than AGPRs.
+    # The prefill's softmax rescales its accumulators on the VALU, which cannot read AGPRs:
+    # with them in AGPRs every block copied 32 of them out and back (and the kernel ran at
+    # three waves per SIMD instead of four).
     return ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
 
 

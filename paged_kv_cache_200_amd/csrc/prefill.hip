@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kLdsThreads) void prefill_lds_kernel(
   constexpr int kRows = kMembers * G;
   constexpr int kGroupTokens = kMembers * kR * kLdsWaves;
   __shared__ LdsStage<D> stage[3];
-  __shared__ int s_ids[kWave];
+  __shared__ int s_ids[kLdsThreads];
   const int s = blockIdx.y;
   const int kvh = blockIdx.z;
   const int tid = threadIdx.x;
@@ -186,23 +186,25 @@ __global__ __launch_bounds__(kLdsThreads) void prefill_lds_kernel(
     }
     mfma_rows_init<D>(rows[r]);
   }
+  // The query loads above are conditional; without this wait the compiler cannot prove
+  // them complete at the block loop's head and waits for every outstanding load (the
+  // staged blocks' too) before each block's first matrix product.
+  __builtin_amdgcn_s_waitcnt(0);
 
   const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
   const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
   const int32_t* trow = tables + static_cast<size_t>(s) * W;
-  // Block ids, 64 at a time: wave 0 fetches them into LDS; the barrier that publishes a
-  // staged block also publishes the ids of the blocks after it.
+  // Block ids, a window of kLdsThreads at a time (one per thread), in LDS.  Each window
+  // is streamed on its own, so the block loop itself holds no table read.
   auto block_ptr = [&](int id, const uint16_t* base) {
     return base + static_cast<size_t>(id) * block_elems + kvh * head_elems;
   };
   auto fetch_ids = [&](int from) {
-    if (wave == 0) {
-      const int k = from + lane;
-      int id = k < nblk ? trow[k] : 0;
-      const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
-      if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-      s_ids[lane] = bad ? 0 : id;
-    }
+    const int k = from + tid;
+    const int id = k < nblk ? trow[k] : 0;
+    const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
+    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+    s_ids[tid] = bad ? 0 : id;
   };
   auto compute = [&](const LdsStage<D>& st, int b) {
     const int t_base = b * kBlockTokens;
@@ -216,40 +218,43 @@ __global__ __launch_bounds__(kLdsThreads) void prefill_lds_kernel(
   };
 
   // Three LDS stages, three register sets: the loads of block j are issued two blocks
-  // before it is stored to LDS (block j lives in stage j % 3).
-  auto issue = [&](int j, StageRegs<D>& r) {
-    if (j % kWave == 0 && j > 0) {
-      __syncthreads();  // every thread has read the previous ids
-      fetch_ids(j);
+  // before it is stored to LDS (block j lives in stage (j - w0) % 3).  Past the window's
+  // last block that block is loaded and stored again (a cache hit, never read): every
+  // load and store of the loop is then unconditional, so the compiler's wait before a
+  // stage store counts only the loads that filled it, not the ones issued after.
+  StageRegs<D> r0, r1, r2;
+  for (int w0 = 0; w0 < nblk; w0 += kLdsThreads) {
+    const int w1 = min(nblk, w0 + kLdsThreads);
+    __syncthreads();  // the previous window's ids and stages are no longer read
+    fetch_ids(w0);
+    __syncthreads();
+    auto issue = [&](int j, StageRegs<D>& r) {
+      // uniform: the block's base address is computed on the scalar unit
+      const int id = __builtin_amdgcn_readfirstlane(s_ids[min(j, w1 - 1) - w0]);
+      stage_load<D>(r, block_ptr(id, kc), block_ptr(id, vc), tid);
+    };
+    issue(w0, r0);
+    issue(w0 + 1, r1);
+    issue(w0 + 2, r2);
+    stage_store<D>(stage[0], r0, tid);
+    __syncthreads();
+    for (int b = w0; b < w1; b += 3) {
+      // stage[0] holds block b; r1, r2 hold blocks b + 1, b + 2 in flight
+      issue(b + 3, r0);
+      compute(stage[0], b);
+      stage_store<D>(stage[1], r1, tid);
+      __syncthreads();
+      if (b + 1 >= w1) break;
+      issue(b + 4, r1);
+      compute(stage[1], b + 1);
+      stage_store<D>(stage[2], r2, tid);
+      __syncthreads();
+      if (b + 2 >= w1) break;
+      issue(b + 5, r2);
+      compute(stage[2], b + 2);
+      stage_store<D>(stage[0], r0, tid);
       __syncthreads();
     }
-    const int id = s_ids[j % kWave];
-    stage_load<D>(r, block_ptr(id, kc), block_ptr(id, vc), tid);
-  };
-  StageRegs<D> r0, r1, r2;
-  fetch_ids(0);
-  __syncthreads();
-  if (nblk > 0) issue(0, r0);
-  if (nblk > 1) issue(1, r1);
-  if (nblk > 2) issue(2, r2);
-  if (nblk > 0) stage_store<D>(stage[0], r0, tid);
-  __syncthreads();
-  for (int b = 0; b < nblk; b += 3) {
-    // stage[0] holds block b; r1, r2 hold blocks b + 1, b + 2 in flight
-    if (b + 3 < nblk) issue(b + 3, r0);
-    compute(stage[0], b);
-    if (b + 1 < nblk) stage_store<D>(stage[1], r1, tid);
-    __syncthreads();
-    if (b + 1 >= nblk) break;
-    if (b + 4 < nblk) issue(b + 4, r1);
-    compute(stage[1], b + 1);
-    if (b + 2 < nblk) stage_store<D>(stage[2], r2, tid);
-    __syncthreads();
-    if (b + 2 >= nblk) break;
-    if (b + 5 < nblk) issue(b + 5, r2);
-    compute(stage[2], b + 2);
-    if (b + 3 < nblk) stage_store<D>(stage[0], r0, tid);
-    __syncthreads();
   }
 
   // Row c's totals live on the four lanes with lane % 16 == c; output row 4h + i's on
