@@ -259,7 +259,6 @@ __device__ __forceinline__ unsigned mfma_tile(
   const int nw = nblk > wave ? (nblk - wave + kTileWaves - 1) / kTileWaves : 0;
   unsigned mism = 0;  // members whose ids differ on this wave's blocks
   // Block ids of this wave's blocks, 64 at a time, one per lane.
-  int id_base = 0;
   auto fetch_ids = [&](int from) -> int {
     const int k = from + lane;
     const bool live = k < nw;
@@ -279,12 +278,12 @@ __device__ __forceinline__ unsigned mfma_tile(
     return id;
   };
   int ids = fetch_ids(0);
-  auto load = [&](MfmaBlock<D>& bl, int k) {  // called with k = 0, 1, 2, ... in order
-    if (k - id_base >= kWave) {
-      id_base += kWave;
-      ids = fetch_ids(id_base);
-    }
-    const int id = __builtin_amdgcn_readlane(ids, k - id_base);
+  // The query loads above are conditional: without this wait the compiler cannot prove
+  // them complete at the block loop's head and waits there for every outstanding load,
+  // the block in flight included.
+  __builtin_amdgcn_s_waitcnt(0);
+  auto load = [&](MfmaBlock<D>& bl, int k) {  // block k of the current id window
+    const int id = __builtin_amdgcn_readlane(ids, k);
     const size_t off = static_cast<size_t>(id) * block_elems + kvh * head_elems;
     mfma_load_block<D>(bl, kc + off, vc + off, c, h);
   };
@@ -292,15 +291,28 @@ __device__ __forceinline__ unsigned mfma_tile(
     const int t_base = (b0 + wave + kTileWaves * k) * kBlockTokens;  // token of slot 0
     mfma_rows_block<D>(rows, cur, qr, t_base, n_c, n_max, h, scale_log2);
   };
-  // Two blocks in flight: the next block's loads are issued before this one's math.
+  // Two blocks in flight: the next block's loads are issued before this one's math.  The
+  // loads of the steady loop are unconditional (a conditional one would make the
+  // compiler's wait before the math cover the block in flight too); each window of 64
+  // blocks, one id per lane, is streamed on its own.
   MfmaBlock<D> bufa, bufb;
-  if (nw > 0) load(bufa, 0);
-  for (int k = 0; k < nw; k += 2) {
-    if (k + 1 < nw) load(bufb, k + 1);
-    process(bufa, k);
-    if (k + 1 < nw) {
-      if (k + 2 < nw) load(bufa, k + 2);
-      process(bufb, k + 1);
+  for (int wb = 0; wb < nw; wb += kWave) {
+    if (wb > 0) ids = fetch_ids(wb);
+    const int n = min(kWave, nw - wb);
+    load(bufa, 0);
+    int k = 0;  // window block k is in bufa
+    for (; k + 2 < n; k += 2) {
+      load(bufb, k + 1);
+      process(bufa, wb + k);
+      load(bufa, k + 2);
+      process(bufb, wb + k + 1);
+    }
+    if (n - k == 2) {
+      load(bufb, k + 1);
+      process(bufa, wb + k);
+      process(bufb, wb + k + 1);
+    } else {
+      process(bufa, wb + k);
     }
   }
   float l_c = rows.l_part;
