@@ -32,7 +32,6 @@ constexpr int kMfmaRows = 16;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct MfmaGeom {
@@ -146,7 +145,11 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
   }
   // P V on the bf16 MFMA with P split into two bf16 terms, hi = P truncated and
   // lo = (P - hi) truncated (P - hi is exact in fp32), so the product sees P to about
-  // 2^-16 relative.  A operand: P[row c][tokens 4h .. 4h + 3], the lane's own scores.
+  // 2^-16 relative.  Both terms go through one 16x16x32 product: its 32-long k runs over
+  // (term, token) pairs, lane (c, h) supplying k = 8h .. 8h + 7 as P_hi[c][4h .. 4h + 3]
+  // then P_lo[c][4h .. 4h + 3] (the lane's own scores), and the B operand of lane
+  // (n, h) the matching V[4h .. 4h + 3][n] twice.  Any order of k is the same sum, so
+  // no lane needs another lane's scores.
   // (v_perm_b32 byte selects: kHighHalves packs the high 16 bits of two words, low word
   // first; kLowHalves their low 16 bits.)
   uint32_t pw[4], rw[4];
@@ -155,12 +158,11 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
     pw[i] = __float_as_uint(p[i]);
     rw[i] = __float_as_uint(p[i] - __uint_as_float(pw[i] & 0xffff0000u));  // exact remainder
   }
-  const i16x4_t a_hi = __builtin_bit_cast(
-      i16x4_t, u32x2_t{__builtin_amdgcn_perm(pw[1], pw[0], kHighHalves),
-                       __builtin_amdgcn_perm(pw[3], pw[2], kHighHalves)});
-  const i16x4_t a_lo = __builtin_bit_cast(
-      i16x4_t, u32x2_t{__builtin_amdgcn_perm(rw[1], rw[0], kHighHalves),
-                       __builtin_amdgcn_perm(rw[3], rw[2], kHighHalves)});
+  const bf16x8_t a = __builtin_bit_cast(
+      bf16x8_t, u32x4_t{__builtin_amdgcn_perm(pw[1], pw[0], kHighHalves),
+                        __builtin_amdgcn_perm(pw[3], pw[2], kHighHalves),
+                        __builtin_amdgcn_perm(rw[1], rw[0], kHighHalves),
+                        __builtin_amdgcn_perm(rw[3], rw[2], kHighHalves)});
   // Tokens past every taken row's end hold stale data: zero their V (0 * NaN).
   if (t_base + kBlockTokens > n_max) {
 #pragma unroll
@@ -172,20 +174,17 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
   }
   const auto& v = cur.v;
   // B operand of tile j: V[tokens 4h .. 4h + 3][dim c * D/16 + j], the even tiles from
-  // the low halves of the lane's words, the odd ones from the high halves.  The two
-  // tiles of a word alternate, so a product never waits on the one just before it.
+  // the low halves of the lane's words, the odd ones from the high halves.
 #pragma unroll
   for (int w = 0; w < Mg::kVWords; ++w) {
-    const i16x4_t b_even = __builtin_bit_cast(
-        i16x4_t, u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], kLowHalves),
-                         __builtin_amdgcn_perm(v[3][w], v[2][w], kLowHalves)});
-    const i16x4_t b_odd = __builtin_bit_cast(
-        i16x4_t, u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], kHighHalves),
-                         __builtin_amdgcn_perm(v[3][w], v[2][w], kHighHalves)});
-    r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_even, r.o[2 * w], 0, 0, 0);
-    r.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, b_odd, r.o[2 * w + 1], 0, 0, 0);
-    r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_even, r.o[2 * w], 0, 0, 0);
-    r.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, b_odd, r.o[2 * w + 1], 0, 0, 0);
+    const uint32_t e0 = __builtin_amdgcn_perm(v[1][w], v[0][w], kLowHalves);
+    const uint32_t e1 = __builtin_amdgcn_perm(v[3][w], v[2][w], kLowHalves);
+    const uint32_t o0 = __builtin_amdgcn_perm(v[1][w], v[0][w], kHighHalves);
+    const uint32_t o1 = __builtin_amdgcn_perm(v[3][w], v[2][w], kHighHalves);
+    const bf16x8_t b_even = __builtin_bit_cast(bf16x8_t, u32x4_t{e0, e1, e0, e1});
+    const bf16x8_t b_odd = __builtin_bit_cast(bf16x8_t, u32x4_t{o0, o1, o0, o1});
+    r.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b_even, r.o[2 * w], 0, 0, 0);
+    r.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b_odd, r.o[2 * w + 1], 0, 0, 0);
   }
 }
 

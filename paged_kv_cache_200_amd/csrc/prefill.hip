@@ -131,7 +131,7 @@ __device__ __forceinline__ void stage_read(MfmaBlock<D>& b, const LdsStage<D>& s
 }
 
 template <int D, int G, int kR>
-__global__ __launch_bounds__(kLdsThreads) void prefill_lds_kernel(
+__global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens, int total_q,
