@@ -539,7 +539,9 @@ def main():
     step_bytes = layers * (p1_bytes + append_bytes)
     value = step_bytes / step_s / 1e9
     achieved = p1_bytes / pass1_s / 1e9
-    traffic = traffic_from_profile() if args.workload == "high_concurrency" and P == 4096 else None
+    # the counters were taken on the seed-0 instance of this workload only
+    traffic = (traffic_from_profile()
+               if args.workload == "high_concurrency" and P == 4096 and args.seed == 0 else None)
 
     probe = None if args.no_copy_probe else copy_probe(torch)
 
