@@ -172,6 +172,22 @@ def test_block_and_partition_boundaries(kv_dtype, hq, hkv, d, P):
     assert_no_device_error()
 
 
+# A wave reads its block ids 64 at a time; with four waves a unit longer than 4096 tokens
+# (P = 0, or a large partition) crosses id windows, with odd and even block counts left
+# for the last window and a partial last block.
+WINDOW_LENS = [9000, 8193, 4112, 4097, 4096, 300]
+
+
+@pytest.mark.parametrize("kv_dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f32", 8, 2, 64),
+                                               ("bf16", 14, 2, 64)])
+@pytest.mark.parametrize("P", [0, 8192])
+def test_units_across_id_windows(kv_dtype, hq, hkv, d, P):
+    case = build_case("windows", WINDOW_LENS, hq, hkv, d, kv_dtype, seed=hq + d + P + 7)
+    assert_parity(run_decode(DeviceCase(case), P), oracle_decode(case), kv_dtype,
+                  f"id windows {kv_dtype} G{hq // hkv} D{d} P{P}")
+    assert_no_device_error()
+
+
 @pytest.mark.parametrize("P", [0, 32])
 def test_empty_contexts(P):
     case = build_case("empty", [0, 5, 0, 40, 0], 8, 2, 64, "bf16", seed=1)

@@ -71,6 +71,20 @@ def test_long_prompts(kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_contexts_across_id_windows(kv_dtype):
+    """The LDS kernel reads block ids 256 at a time: contexts of more than 4096 tokens
+    cross that window, with the chunk inside the second window or across the boundary."""
+    lens = [5200, 4200, 4111]
+    chunks = [100, 37, 200]
+    say(f"prefill id windows {kv_dtype}")
+    case, q, cu = _case(lens, chunks, 16, 4, 128, kv_dtype, seed=41)
+    want = pp.paged_prefill(q, case.k_pool[0], case.v_pool[0], case.block_tables, cu,
+                            case.context_lens, case.scale, kv_dtype)
+    assert_parity(_run(case, q, cu), want, kv_dtype, f"prefill id windows {kv_dtype}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
 def test_one_token_chunks_equal_decode(kv_dtype):
     from paged_kv_cache_200_amd import ops
     case = build_case("dec", [1, 5, 16, 17, 200, 513], 16, 4, 128, kv_dtype, seed=5)

@@ -66,6 +66,24 @@ def test_mixed_groups(P, kv_dtype, hq, hkv, d, round_up):
     assert_no_device_error()
 
 
+@pytest.mark.parametrize("P", [0, 8192])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_long_shared_prefix_across_id_windows(P, kv_dtype):
+    """A shared prefix of more than 4096 tokens: the matrix-core tile reads 64 block ids
+    per wave at a time (256 per tile), so its shared range crosses id windows."""
+    say(f"long shared prefix P={P} {kv_dtype}")
+    prefixes = [5008, 4112]
+    forks = [3, 2]
+    privates = [[7, 0, 130], [33, 1]]
+    case = fork_case("longshared", prefixes, forks, privates, 16, 4, 128, kv_dtype, seed=P + 5)
+    starts = np.concatenate([[0], np.cumsum(forks)])
+    shared = [n // 16 for n in prefixes]
+    dc = DeviceCase(case)
+    assert_parity(_shared_decode(dc, starts, shared, P), oracle_decode(case), kv_dtype,
+                  f"long shared prefix P{P}")
+    assert_no_device_error()
+
+
 def test_wrong_hint_and_clamp_still_exact():
     """A sharing hint that is not true (members hold different blocks), a bound below the
     hint, and members shorter than the declared prefix: results stay the plain decode."""
