@@ -98,6 +98,19 @@ __device__ __forceinline__ void mfma_rows_init(MfmaRows<D>& r) {
 // P enters P V as two bf16 terms (truncated value + truncated remainder, about 2^-16
 // relative).  (A single rounded bf16 term measured 8% faster in the prefill but put the
 // error at 4e-3, a thousand times higher.)
+// Max over the four lanes that hold one score row (c, c + 16, c + 32, c + 48) with the
+// gfx950 lane swaps, which stay in the VALU (a shuffle goes through the LDS crossbar).
+// After the 32-lane swap a lane holds the max of itself and lane ^ 32; after the 16-lane
+// swap, of its 16-apart partner too.
+__device__ __forceinline__ float max_over_h(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int D>
 __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cur,
                                                 const u32x4_t (&qr)[MfmaGeom<D>::kQkSteps],
@@ -119,8 +132,7 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
     x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
     bm = fmaxf(bm, x[i]);
   }
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = max_over_h(bm);
   const bool raise = bm > r.m_c + kLazyMaxSlack;
   if (__any(raise)) {
     float a = 1.0f;
