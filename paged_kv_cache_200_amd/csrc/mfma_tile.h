@@ -98,17 +98,28 @@ __device__ __forceinline__ void mfma_rows_init(MfmaRows<D>& r) {
 // P enters P V as two bf16 terms (truncated value + truncated remainder, about 2^-16
 // relative).  (A single rounded bf16 term measured 8% faster in the prefill but put the
 // error at 4e-3, a thousand times higher.)
-// Max over the four lanes that hold one score row (c, c + 16, c + 32, c + 48) with the
-// gfx950 lane swaps, which stay in the VALU (a shuffle goes through the LDS crossbar).
-// After the 32-lane swap a lane holds the max of itself and lane ^ 32; after the 16-lane
-// swap, of its 16-apart partner too.
-__device__ __forceinline__ float max_over_h(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+// x combined with the value of lane ^ 16, then of lane ^ 32 (gfx950 lane swaps, in the
+// VALU).  A swap returns the lane's own value and its partner's in some order; the sum
+// and the max are commutative, so each step equals x op x[lane ^ k] bit for bit.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int D>
@@ -132,7 +143,7 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
     x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
     bm = fmaxf(bm, x[i]);
   }
-  bm = max_over_h(bm);
+  bm = max_xor32(max_xor16(bm));  // the row's four lanes c + 16 h
   const bool raise = bm > r.m_c + kLazyMaxSlack;
   if (__any(raise)) {
     float a = 1.0f;
@@ -327,8 +338,7 @@ __device__ __forceinline__ unsigned mfma_tile(
     }
   }
   float l_c = rows.l_part;
-  l_c += __shfl_xor(l_c, 16);
-  l_c += __shfl_xor(l_c, 32);
+    l_c = sum_xor32(sum_xor16(l_c));
   const float m_c = rows.m_c;
   const auto& o = rows.o;
 

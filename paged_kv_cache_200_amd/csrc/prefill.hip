@@ -262,8 +262,7 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     float l_c = rows[r].l_part;
-    l_c += __shfl_xor(l_c, 16);
-    l_c += __shfl_xor(l_c, 32);
+        l_c = sum_xor32(sum_xor16(l_c));
     const int t0 = tg + (wave * kR + r) * kMembers;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
