@@ -490,9 +490,8 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
 
-    # the first pass alone, in the step's work order: partial outputs when the context is
-    # split, else the planned decode, which is then that single launch
-    np_max = max(1, -(-max_ctx // P)) if P > 0 else 1
+    # the first pass alone, as the step launches it: the planned decode on a plan computed
+    # beforehand is that single launch (split sequences are merged inside it)
     plan_ws = pkv.decode_plan(ctx, tables, hq, d, max_ctx, P)
     timed_kernel = "decode_pass1_kernel"
     if shared_path:
@@ -502,14 +501,6 @@ def main():
 
         def pass1():
             shared_decode(0)
-    elif np_max > 1:
-        part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
-        part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
-
-        def pass1():
-            pkv.paged_decode_partials(q, kc, vc, tables, ctx, max_ctx, P, scale=scale,
-                                      part_out=part_out, part_lse=part_lse,
-                                      plan_workspace=plan_ws)
     else:
         def pass1():
             pkv.paged_decode_planned(q, kc, vc, tables, ctx, max_ctx, plan_ws, scale=scale,
@@ -580,8 +571,8 @@ def main():
             "step": ("append + work plan (one launch), shared-prefix and private ranges (one "
                      "launch), LSE combine"
                      if shared_path else
-                     "append 1 token/seq + work plan (one launch), split-KV first pass, "
-                     "LSE combine"),
+                     "append 1 token/seq + work plan (one launch), split-KV first pass with "
+                     "the LSE merge of split sequences in the same launch"),
             "appended_tokens_per_layer": total_new,
             "launch": "hip graph of the whole step" if args.graph else "eager",
         },

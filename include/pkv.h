@@ -121,8 +121,8 @@ int pkv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v
  * the work plan (a count and batch * P unit entries) and, when the context is
  * split into P = ceil(max_context_len / partition_size) > 1 partitions, the
  * per-partition partial outputs and log-sum-exps, batch * num_q_heads * P *
- * (head_dim + 1) floats; each part 256-byte aligned.  The workspace itself
- * must be 256-byte aligned.
+ * (head_dim + 1) floats, and batch * num_q_heads int32 merge counters; each
+ * part 256-byte aligned.  The workspace itself must be 256-byte aligned.
  */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
@@ -130,7 +130,8 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
 /*
  * Work plan of the decode's first pass, written into `workspace`: the
  * (sequence, partition) units in longest-first order (every full partition,
- * then each sequence's shorter last partition by decreasing length).  The
+ * then the last partition of every split sequence, so that its merge is done
+ * early, then the other sequences by decreasing length).  The
  * order decides only which workgroup runs when; results never depend on it.
  * Reads context_lens; lengths are clamped to bt_stride * 16.  A plan stays
  * valid for every pkv_paged_decode_planned call with the same context_lens
@@ -159,14 +160,20 @@ int pkv_decode_plan(void* workspace, size_t workspace_bytes, const int32_t* cont
  * partition_size = 0: one pass per (sequence, KV head) over the whole
  * context.  partition_size = P > 0 (multiple of 16): the context is split
  * into partitions of P tokens, each attended independently, then merged by
- * their log-sum-exps (a second kernel on the same stream); sequences that
- * fit in one partition are written directly.  The result does not depend on
+ * their log-sum-exps, in the same launch: the last of a sequence's partition
+ * workgroups to finish (a per-(sequence, KV head) counter in the workspace)
+ * merges them, with the arithmetic and order of pkv_lse_combine, so the
+ * result equals pkv_paged_decode_partials followed by pkv_lse_combine bit for
+ * bit.  Past 8 partitions per sequence the merge is a second launch (the
+ * combine kernel, same result), whose rows run in parallel.  Sequences that
+ * fit in one partition are written directly.  Calls
+ * that overlap in time must not share a workspace.  The result does not depend on
  * the batch: a sequence decoded alone or in any batch, with the same
  * partition_size, gives bit-identical out and lse.
  * lse may be NULL.  workspace: pkv_decode_workspace_bytes(...) bytes,
  * 256-byte aligned, owned by the caller; its previous contents do not matter.
- * Launches, on `stream`: the plan kernel, the first pass, and (when split)
- * the combine.
+ * Launches, on `stream`: the plan kernel (which also zeroes the merge
+ * counters), the first pass, and past 8 partitions the combine.
  */
 int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* block_tables, int64_t bt_stride,
@@ -181,8 +188,8 @@ int pkv_paged_decode(float* out, float* lse, const void* q, const void* k_cache,
  * k_new, v_new, block_tables, bt_stride, start_pos, cu_new_tokens, batch,
  * total_new, ...) followed by pkv_paged_decode(...) on the same stream, with
  * the same arguments, results and errors.  The append and the work plan share
- * one launch (they touch disjoint memory), then come the first pass and,
- * when split, the combine.  context_lens must already count the appended
+ * one launch (they touch disjoint memory), then comes the first pass, which
+ * also merges split sequences.  context_lens must already count the appended
  * tokens; the caller advances lengths, never the library.
  */
 int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache, void* v_cache,
@@ -314,6 +321,8 @@ int pkv_paged_decode_partials(float* part_out, float* part_lse, const void* q,
  * order from a plan that pkv_decode_plan wrote earlier (same stream order)
  * into the same workspace for the same context_lens contents, batch,
  * max_context_len and partition_size.  Results are those of pkv_paged_decode.
+ * One launch: the merge counters that pkv_decode_plan zeroed are reset by each
+ * call's merging workgroups, so any number of planned calls may follow a plan.
  */
 int pkv_paged_decode_planned(float* out, float* lse, const void* q, const void* k_cache,
                              const void* v_cache, const int32_t* block_tables, int64_t bt_stride,

@@ -55,7 +55,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D>
+// kAgent: read the partial results through device-scope loads (global_load ... sc1), which
+// miss in this XCD's L2 when another XCD wrote them in the same launch; else plain loads.
+template <bool kAgent>
+__device__ __forceinline__ float load_partial(const float* p) {
+  if constexpr (kAgent)
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+template <int D, bool kAgent = false>
 __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* __restrict__ lse_el,
                                             const float* __restrict__ pl,
                                             const float* __restrict__ po, int nparts, int lane) {
@@ -63,14 +73,14 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
   constexpr float kLog2e = 1.44269504088896340736f;
   float M = -INFINITY;
   for (int p0 = 0; p0 < nparts; p0 += kWave)
-    M = fmaxf(M, wave_max(p0 + lane < nparts ? pl[p0 + lane] : -INFINITY));
+    M = fmaxf(M, wave_max(p0 + lane < nparts ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY));
   float acc[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
   float den = 0.0f;
   for (int p0 = 0; p0 < nparts; p0 += kWave) {
     const int cnt = min(kWave, nparts - p0);
-    const float lp = lane < cnt ? pl[p0 + lane] : -INFINITY;
+    const float lp = lane < cnt ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY;
     const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
     den += wave_sum(w);
     int p = 0;
@@ -81,7 +91,8 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
       for (int u = 0; u < 4; ++u) {
         wp[u] = __shfl(w, p + u);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) x[u][j] = po[(p0 + p + u) * D + j * kWave + lane];
+        for (int j = 0; j < kPer; ++j)
+          x[u][j] = load_partial<kAgent>(po + (p0 + p + u) * D + j * kWave + lane);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -91,7 +102,8 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
     for (; p < cnt; ++p) {
       const float wp = __shfl(w, p);
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp, po[(p0 + p) * D + j * kWave + lane], acc[j]);
+      for (int j = 0; j < kPer; ++j)
+        acc[j] = fmaf(wp, load_partial<kAgent>(po + (p0 + p) * D + j * kWave + lane), acc[j]);
     }
   }
 #pragma unroll
@@ -168,11 +180,13 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
     int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2, int part_tokens,
     int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
     float* __restrict__ out, float* __restrict__ lse, int order,
-    const int4* __restrict__ plan, const int* __restrict__ plan_count) {
+    const int4* __restrict__ plan, const int* __restrict__ plan_count,
+    const int32_t* __restrict__ nslots, int* __restrict__ merge_ctr) {
   using Gm = Geom<T, D>;
   int part, kvh, s;  // part: the partial-result slot written unless `direct`
   int tok0, tok1;    // the unit's token range
   bool direct;       // the unit is its sequence's only one: write out / lse
+  bool merge = false;  // a split unit whose sequence is merged in this launch
   const bool leader = threadIdx.x == 0;
   if (order == kOrderPlanned) {
     // The plan entry carries the unit's (range-checked) token range and slot: one load
@@ -186,6 +200,7 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
     tok1 = u.z;
     part = u.w & kSlotMask;
     direct = (u.w & kDirectFlag) != 0 && out != nullptr;
+    merge = !direct && merge_ctr != nullptr && out != nullptr;
   } else {
     int nx_parts;
     if (order == kOrderPartMinor) {
@@ -265,6 +280,8 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
         }
       }
     }
+    // slots of a split sequence; the last of its units to finish merges them
+    const int n_merge = merge ? min(nslots[s], max_parts) : 0;
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
       const int g = idx / D;
@@ -285,9 +302,41 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
       if (direct) {
         out[sh * D + d] = o;
         if (lse != nullptr && d == 0) lse[sh] = ls;
+      } else if (n_merge > 0) {
+        // device-scope stores (global_store ... sc1): written through to where every XCD's
+        // device-scope loads see them, so the merging workgroup needs no cache flush
+        float* po = part_out + (sh * max_parts + part) * D + d;
+        __hip_atomic_store(po, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(part_lse + sh * max_parts + part, ls, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       } else {
         part_out[(sh * max_parts + part) * D + d] = o;
         if (d == 0) part_lse[sh * max_parts + part] = ls;
+      }
+    }
+    // (marked unlikely: with the merge on the cold path the register allocation of the
+    // block loop matches the kernel without it, which has no spill at 256 VGPRs)
+    if (__builtin_expect(n_merge > 0, 0)) {
+      // Split sequence: the last of its units to finish merges every slot (the log-sum-exp
+      // combine, same routine and order as the combine kernel).  Each thread waits until
+      // its partial stores have completed at device scope, then one ticket per workgroup
+      // is taken from the (sequence, KV head) counter.  The counter is zeroed by the plan
+      // and reset by the merging workgroup, so a reused plan starts from zero too.
+      __shared__ int s_ticket;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      int* ctr = merge_ctr + static_cast<size_t>(s) * num_kv_heads + kvh;
+      if (leader) s_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_ticket == n_merge - 1) {
+        for (int g = wave; g < G; g += NW) {
+          const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
+          combine_row<D, true>(out + sh * D, lse != nullptr ? lse + sh : nullptr,
+                               part_lse + sh * max_parts, part_out + sh * max_parts * D,
+                               n_merge, lane);
+        }
+        if (leader) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -313,9 +362,10 @@ void combine_launch(hipStream_t stream, float* out, float* lse, const float* par
 // each entry {sequence, partition, context length clamped to the table, 0},
 // so the hardware dispatcher, which hands out workgroups in grid order, schedules them
 // like longest-processing-time-first list scheduling.  Every full partition (exactly
-// part_tokens tokens) comes first, in sequence order; then each sequence's last, shorter
-// partition, bucketed by its length in 16-token blocks (>> key_shift), longest bucket
-// first.  part_tokens = 0 means one unit per sequence, bucketed by its whole length.
+// part_tokens tokens) comes first, in sequence order; then the last partition of every
+// split sequence (so its merge happens early); then each other sequence's only unit,
+// bucketed by its length in 16-token blocks (>> key_shift), longest bucket first.
+// part_tokens = 0 means one unit per sequence, bucketed by its whole length.
 // The order only changes which workgroup runs when, never a unit's result.
 // One workgroup; plan holds at most batch * np entries.
 constexpr int kPlanThreads = 1024;
@@ -353,6 +403,8 @@ struct PlanInput {
   const int32_t* group_shared_blocks;
   int num_groups;
   int max_shared_blocks;  // shared lengths are clamped to this and to the table width
+  int* merge_ctr;         // nullable: per (sequence, KV head) merge counters, zeroed here
+  int ctr_count;
 };
 
 // Tokens of group g's shared prefix that the shared pass attends, clamped exactly as the
@@ -431,6 +483,8 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
   const int tid = threadIdx.x;
   s_cursor[tid] = 0;
   if (tid == 0) s_full_total = 0;
+  if (in.merge_ctr != nullptr)
+    for (int i = tid; i < in.ctr_count; i += kPlanThreads) in.merge_ctr[i] = 0;
   const bool lds_starts = in.group_starts != nullptr && in.num_groups <= kPlanLdsGroups;
   if (lds_starts)
     for (int g = tid; g <= in.num_groups; g += kPlanThreads) s_starts[g] = in.group_starts[g];
@@ -445,8 +499,12 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
       if (bad) PKV_FLAG_ERROR(PKV_DEVERR_GROUPS);
     }
   }
-  auto key_of = [&](int len) {
-    return min(kPlanBuckets - 1, ((len + kBlockTokens - 1) / kBlockTokens) >> in.key_shift);
+  // The last unit of a split sequence goes in the first bucket, right after the full
+  // partitions: the sequence's partial results are then complete, and merged, long before
+  // the end of the pass instead of on its critical path.
+  auto key_of = [&](const SeqUnits& u) {
+    if (u.full > 0) return kPlanBuckets - 1;
+    return min(kPlanBuckets - 1, ((u.tail_len + kBlockTokens - 1) / kBlockTokens) >> in.key_shift);
   };
   SeqUnits first = {0, 0, 0, 0, 0, 0};  // this thread's sequence of the first round
   for (int base = 0; base < in.batch; base += kPlanThreads) {
@@ -461,7 +519,7 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
       const int covered = u.base + u.full * P + (u.tail ? u.tail_len : 0);
       if (covered < u.n) PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
       nslots[s] = (u.nsp == 0 && units == 1) ? 0 : u.nsp + units;
-      if (u.tail) atomicAdd(&s_cursor[key_of(u.tail_len)], 1);
+      if (u.tail) atomicAdd(&s_cursor[key_of(u)], 1);
     }
     const int incl = block_scan_inclusive(s_scan, u.full);
     const int first = s_full_total + incl - u.full;
@@ -484,7 +542,7 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
     const SeqUnits u = s == tid ? first : seq_units(in, s, starts);
     if (u.tail) {
       const int t0 = u.base + u.full * P;
-      const int i = atomicAdd(&s_cursor[key_of(u.tail_len)], 1);
+      const int i = atomicAdd(&s_cursor[key_of(u)], 1);
       plan[i] = make_int4(s, t0, t0 + u.tail_len, unit_slot(u, u.full));
     }
   }
@@ -694,7 +752,8 @@ __global__ __launch_bounds__(kTileWaves * kWave) void decode_shared_mfma_kernel(
 
 using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
                           const int32_t*, int, const int32_t*, int, int, int, float, int, int,
-                          float*, float*, float*, float*, const int4*, const int*);
+                          float*, float*, float*, float*, const int4*, const int*,
+                          const int32_t*, int*);
 
 // order = kOrderPlanned: plan/plan_count from plan_kernel, grid of batch * np units.
 template <int NW, typename T, int D, int G>
@@ -702,7 +761,9 @@ void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t st
                   const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                   const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                   int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
-                  float* lse, const int4* plan, const int* plan_count) {
+                  float* lse, const int4* plan, const int* plan_count, const int32_t* nslots,
+                  int* merge_ctr) {
+  static_assert(NW > 1, "split sequences are merged in the multi-wave epilogue");
   dim3 grid;
   if (order == kOrderPlanned)
     grid = dim3(static_cast<unsigned>(num_kv_heads) * batch * np);
@@ -714,7 +775,7 @@ void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t st
                      stream, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
                      part_tokens, max_parts, part_out, part_lse, out, lse, order, plan,
-                     plan_count);
+                     plan_count, nslots, merge_ctr);
 }
 
 // The configuration the library ships: four waves share a (sequence, KV head,
@@ -724,10 +785,11 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
                    const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
                    const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                    int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
-                   float* lse, const int4* plan, const int* plan_count) {
+                   float* lse, const int4* plan, const int* plan_count, const int32_t* nslots,
+                   int* merge_ctr) {
   pass1_launch<4, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx, hq,
                            hkv, nb, scale_log2, part_tokens, max_parts, part_out, part_lse, out,
-                           lse, plan, plan_count);
+                           lse, plan, plan_count, nslots, merge_ctr);
 }
 
 struct SharedArgs {
@@ -847,6 +909,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // partitions of partition_size tokens when that exceeds one (else one unit per sequence,
 // written straight).  Shared-prefix decode: a sequence's slots are the shared prefix's
 // partitions followed by its private range's, at most P + 1.
+// Most partial-result slots per sequence merged inside the first pass (see decode_impl).
+constexpr int kMaxInPassMergeSlots = 8;
+
 struct Geometry {
   int tokens;      // partition size used by the units (0: a whole sequence / range)
   int max_slots;   // partial-result slots per (sequence, query head)
@@ -870,13 +935,15 @@ Geometry decode_geometry(int32_t max_ctx, int32_t partition_size, bool shared) {
 }
 
 // Workspace: [plan count | plan entries (int4, batch * max_slots) | per-sequence slot counts
-// (int32, batch) | partial outputs | partial lse], each part 256-byte aligned.
+// (int32, batch) | partial outputs | partial lse | merge counters (int32, batch * num_q_heads)],
+// each part 256-byte aligned.
 struct Workspace {
   int* plan_count = nullptr;
   int4* plan = nullptr;
   int* nslots = nullptr;
   float* part_out = nullptr;
   float* part_lse = nullptr;
+  int* merge_ctr = nullptr;  // batch * num_q_heads counters (indexed s * Hkv + KV head)
   size_t bytes = 0;
 };
 
@@ -896,6 +963,8 @@ Workspace workspace_layout(void* base, int32_t batch, int32_t hq, int32_t D, con
     off += align_up(rows * D * sizeof(float));
     w.part_lse = reinterpret_cast<float*>(p + off);
     off += align_up(rows * sizeof(float));
+    w.merge_ctr = reinterpret_cast<int*>(p + off);
+    off += align_up(static_cast<size_t>(batch) * hq * sizeof(int));
   }
   w.bytes = off;
   return w;
@@ -912,7 +981,7 @@ int plan_key_shift(int32_t max_context_len, int32_t part_tokens) {
 PlanInput plan_input(const int32_t* ctx, int32_t batch, int cap, const Geometry& g,
                      int32_t max_context_len, const int32_t* group_starts,
                      const int32_t* group_shared_blocks, int32_t num_groups,
-                     int32_t max_shared_blocks) {
+                     int32_t max_shared_blocks, int* merge_ctr = nullptr, int ctr_count = 0) {
   PlanInput in;
   in.ctx = ctx;
   in.batch = batch;
@@ -924,6 +993,8 @@ PlanInput plan_input(const int32_t* ctx, int32_t batch, int cap, const Geometry&
   in.group_shared_blocks = group_shared_blocks;
   in.num_groups = num_groups;
   in.max_shared_blocks = max_shared_blocks;
+  in.merge_ctr = merge_ctr;
+  in.ctr_count = ctr_count;
   return in;
 }
 
@@ -966,11 +1037,18 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
   const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, geo);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int cap = static_cast<int>(bt_stride) * kBlockTokens;
+  // Plain decode merges split sequences inside the first pass when they have few slots.
+  // Past kMaxInPassMergeSlots the merging workgroup's serial walk over the slots costs
+  // more than the combine launch, whose (sequence, head) rows run in parallel; the
+  // shared-prefix kernels always leave the merge to the combine launch.
+  const bool in_pass_merge = !shared && geo.partials && geo.max_slots <= kMaxInPassMergeSlots;
   const PlanInput in = plan_input(context_lens, batch, cap, geo, max_context_len,
                                   shared ? groups->starts : nullptr,
                                   shared ? groups->shared_blocks : nullptr,
                                   shared ? groups->count : 0,
-                                  shared ? groups->max_shared_blocks : 0);
+                                  shared ? groups->max_shared_blocks : 0,
+                                  in_pass_merge ? w.merge_ctr : nullptr,
+                                  in_pass_merge ? batch * num_q_heads : 0);
   if (append != nullptr && append->total > 0) {
     const int eb = elem_bytes(dtype);
     const int wgs = 1 + (append->total + kAppendPerGroup - 1) / kAppendPerGroup;
@@ -1015,13 +1093,10 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
     fn(kOrderPlanned, geo.max_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
        static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
        scale_log2, geo.tokens, geo.max_slots, w.part_out, w.part_lse, out, lse, w.plan,
-       w.plan_count);
+       w.plan_count, w.nslots, in_pass_merge ? w.merge_ctr : nullptr);
     if ((st = launch_status()) != PKV_OK) return st;
   }
-  // A separate second pass: merging inside the first pass would need device-scope
-  // fences (whole-L2 write-back and invalidate per split workgroup), measured to cost
-  // far more than this launch.
-  if (geo.partials) {
+  if (geo.partials && !in_pass_merge) {
     combine_launch(s, out, lse, w.part_out, w.part_lse, context_lens, w.nslots, batch, cap,
                    num_q_heads, head_dim, geo.tokens, geo.max_slots, 1);
     st = launch_status();
@@ -1069,7 +1144,8 @@ extern "C" int pkv_decode_plan(void* workspace, size_t workspace_bytes,
   const Geometry geo = decode_geometry(max_context_len, partition_size, false);
   const Workspace w = workspace_layout(workspace, batch, num_q_heads, head_dim, geo);
   const PlanInput in = plan_input(context_lens, batch, static_cast<int>(bt_stride) * kBlockTokens,
-                                  geo, max_context_len, nullptr, nullptr, 0, 0);
+                                  geo, max_context_len, nullptr, nullptr, 0, 0, w.merge_ctr,
+                                  geo.partials ? batch * num_q_heads : 0);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0,
                      static_cast<hipStream_t>(stream), w.plan, w.plan_count, w.nslots, in);
   return launch_status();
@@ -1229,7 +1305,7 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
   fn(order, grid_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
      static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
      scale_to_log2(scale), partition_size, max_partitions, part_out, part_lse, nullptr, nullptr,
-     plan, plan_count);
+     plan, plan_count, nullptr, nullptr);
   return launch_status();
 }
 

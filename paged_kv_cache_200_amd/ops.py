@@ -164,7 +164,8 @@ def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_contex
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
                  partition_size=0, out=None, lse=None, workspace=None, want_lse=True,
                  stream=None):
-    """Decode attention of q [B, Hq, D] over the paged caches (plan + first pass + combine).
+    """Decode attention of q [B, Hq, D] over the paged caches (plan, then a first pass that
+    also merges the partitions of split sequences).
 
     Returns (out float32 [B, Hq, D], lse float32 [B, Hq] or None).
     max_context_len is a host-side upper bound of context_lens.

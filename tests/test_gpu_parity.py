@@ -351,7 +351,7 @@ def test_partials_with_and_without_plan_identical():
 
 
 @pytest.mark.parametrize("P", [0, 64, 1024])
-def test_plan_lists_every_unit_once_longest_first(P):
+def test_plan_lists_every_unit_once_in_order(P):
     """Plan layout inside the workspace: int32 count at byte 0; from byte 256 int4
     entries (sequence, first token, end token, slot | 1<<30 when the unit is the
     sequence's only one and writes the output itself); then one int32 per sequence,
@@ -384,8 +384,19 @@ def test_plan_lists_every_unit_once_longest_first(P):
             assert [w for _, _, w in units] == list(range(len(want))), s_
             assert nslots[s_] == len(want), s_
     assert count == sum(len(v) for v in per_seq.values())
-    blocks = [-(-(t1 - t0) // 16) for _, t0, t1, _ in ent]
-    assert blocks == sorted(blocks, reverse=True), "plan is not longest-first"
+    # order: every full partition, then the last unit of every split sequence (merged
+    # early), then the other units longest first
+    rank = []
+    for s_, t0, t1, _ in ent:
+        if split and t1 - t0 == P:
+            rank.append(0)
+        elif len(per_seq[s_]) > 1:
+            rank.append(1)
+        else:
+            rank.append(2)
+    assert rank == sorted(rank), "full partitions, then split sequences' last units, first"
+    rest = [-(-(t1 - t0) // 16) for (_, t0, t1, _), r in zip(ent, rank) if r == 2]
+    assert rest == sorted(rest, reverse=True), "plan is not longest-first"
     assert_no_device_error()
 
 
@@ -467,4 +478,42 @@ def test_append_paged_decode_equals_separate_calls(P, kv_dtype):
     want = pa.paged_decode(case.q[0], kp, vp, case.block_tables, case.context_lens, case.scale,
                            kv_dtype)
     assert_parity((o1.cpu().numpy(), l1.cpu().numpy()), want, kv_dtype, f"append+decode P{P}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("wl,P", [("long_context", 512), ("high_concurrency", 1024)])
+def test_in_pass_merge_sees_this_calls_partials(wl, P):
+    """Split sequences are merged inside the first pass by the last of their units to
+    finish, reading the other units' partial results through device-scope loads.  A new
+    query on every call, on one reused workspace and on one reused plan: each result must
+    equal that query's first pass + standalone combine bit for bit, so a merge that read
+    a previous call's partials (or a counter left unreset) fails."""
+    case = config_case(wl, 1, max_batch=64)
+    dc = DeviceCase(case)
+    ops = _ops()
+    rng = np.random.default_rng(P)
+    need = ops.decode_workspace_bytes(case.batch, case.num_q_heads, case.head_dim, dc.max_ctx, P)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    plan_ws = ops.decode_plan(dc.ctx, dc.tables, case.num_q_heads, case.head_dim, dc.max_ctx, P)
+    for i in range(6):
+        qh = rng.standard_normal(case.q[0].shape).astype(np.float32)
+        if case.kv_dtype == "bf16":
+            qh = bf16_bits(qh)
+        q = dev(qh)
+        say(f"  {wl} P{P} call {i}")
+        if i % 2 == 0:
+            o, l = ops.paged_decode(q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                                    scale=float(case.scale), partition_size=P, workspace=ws)
+        else:
+            o, l = ops.paged_decode_planned(q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
+                                            plan_ws, scale=float(case.scale), partition_size=P)
+        po, pl = ops.paged_decode_partials(q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx, P,
+                                           scale=float(case.scale))
+        so, sl = ops.lse_combine(po, pl, dc.ctx, P)
+        torch.cuda.synchronize()
+        assert o.cpu().numpy().tobytes() == so.cpu().numpy().tobytes(), f"call {i}"
+        assert l.cpu().numpy().tobytes() == sl.cpu().numpy().tobytes(), f"call {i}"
+        if i == 5:
+            assert_parity((o.cpu().numpy(), l.cpu().numpy()), oracle_decode(case, q=qh),
+                          case.kv_dtype, f"{wl} P{P}")
     assert_no_device_error()
