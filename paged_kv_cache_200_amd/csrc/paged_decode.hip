@@ -65,7 +65,15 @@ __device__ __forceinline__ float load_partial(const float* p) {
     return *p;
 }
 
-template <int D, bool kAgent = false>
+// Most partial-result slots per sequence merged inside the first pass (decode_impl
+// launches the combine kernel past that).
+constexpr int kMaxInPassMergeSlots = 8;
+
+// kChunk: partitions whose partial outputs are loaded together, before their weighted
+// sum (16 in the combine kernel; 4 in the merge inside the first pass, which keeps that
+// kernel's register allocation).  The sum runs over the partitions in order whatever the
+// chunk, so both give the same bits.
+template <int D, bool kAgent = false, int kChunk = 16>
 __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* __restrict__ lse_el,
                                             const float* __restrict__ pl,
                                             const float* __restrict__ po, int nparts, int lane) {
@@ -84,18 +92,18 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
     const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
     den += wave_sum(w);
     int p = 0;
-    for (; p + 4 <= cnt; p += 4) {
-      float wp[4];
-      float x[4][kPer];
+    for (; p + kChunk <= cnt; p += kChunk) {
+      float wp[kChunk];
+      float x[kChunk][kPer];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kChunk; ++u) {
         wp[u] = __shfl(w, p + u);
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
           x[u][j] = load_partial<kAgent>(po + (p0 + p + u) * D + j * kWave + lane);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kChunk; ++u)
 #pragma unroll
         for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp[u], x[u][j], acc[j]);
     }
@@ -332,9 +340,9 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
       if (s_ticket == n_merge - 1) {
         for (int g = wave; g < G; g += NW) {
           const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
-          combine_row<D, true>(out + sh * D, lse != nullptr ? lse + sh : nullptr,
-                               part_lse + sh * max_parts, part_out + sh * max_parts * D,
-                               n_merge, lane);
+          combine_row<D, true, 4>(
+              out + sh * D, lse != nullptr ? lse + sh : nullptr, part_lse + sh * max_parts,
+              part_out + sh * max_parts * D, n_merge, lane);
         }
         if (leader) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -909,9 +917,6 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // partitions of partition_size tokens when that exceeds one (else one unit per sequence,
 // written straight).  Shared-prefix decode: a sequence's slots are the shared prefix's
 // partitions followed by its private range's, at most P + 1.
-// Most partial-result slots per sequence merged inside the first pass (see decode_impl).
-constexpr int kMaxInPassMergeSlots = 8;
-
 struct Geometry {
   int tokens;      // partition size used by the units (0: a whole sequence / range)
   int max_slots;   // partial-result slots per (sequence, query head)
