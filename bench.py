@@ -31,7 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_high_concurrency.json")
+# HBM traffic records (rocprofv3 counters) of the first pass, per workload
+TRAFFIC_FILES = {w: os.path.join(ROOT, "profiles", f"traffic_{w}.json")
+                 for w in ("high_concurrency", "long_context")}
 # the sources that define the first pass (and the plan/append prologue of its step);
 # counters taken on other sources are not reported
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
@@ -68,6 +70,10 @@ def parse_args():
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="decode fork workloads with the plain path (each fork re-reads the "
                         "shared prefix) instead of the shared-prefix path")
+    p.add_argument("--cold", action="store_true",
+                   help="write a 1 GiB scratch buffer before every timed step (outside the "
+                        "timed region), so no step finds the previous one's data in the L2 "
+                        "or the 256 MB Infinity Cache; each step is then timed on its own")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="before the timed steps, run 3 device copies of MIB MiB (a known-size "
                         "reference for HBM traffic counters)")
@@ -104,14 +110,19 @@ def copy_probe(torch, nbytes=2 << 30, reps=10):
     return 2 * nbytes / sec / 1e9
 
 
-def traffic_from_profile():
-    """HBM bytes per launch from committed PMC counters, if taken on this kernel source."""
+def traffic_from_profile(workload, partition_size, seed):
+    """HBM bytes per launch from committed PMC counters, if taken on this kernel source,
+    workload, partition size and seed."""
+    path = TRAFFIC_FILES.get(workload)
+    if path is None:
+        return None
     try:
-        info = json.load(open(TRAFFIC_FILE))
-        if info.get("kernel_source_sha256") == decode_source_digest():
-            return info.get("bytes_per_launch")
+        info = json.load(open(path))
     except (OSError, ValueError):
-        pass
+        return None
+    if (info.get("kernel_source_sha256") == decode_source_digest()
+            and info.get("partition_size") == partition_size and info.get("seed") == seed):
+        return info.get("bytes_per_launch")
     return None
 
 
@@ -476,23 +487,44 @@ def main():
         raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
 
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        run()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
+    if args.cold:
+        # every step on its own, after a 1 GiB write that evicts L2 and Infinity Cache
+        # (no host synchronisation between steps: while the GPU writes the scratch buffer
+        # the host enqueues the step, so no step waits for its own launches)
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        marks = []
+        for i in range(args.steps):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            marks.append((e0, e1))
+        torch.cuda.synchronize()
+        per_step = np.array([e0.elapsed_time(e1) for e0, e1 in marks])
+        ms_per_step = float(np.mean(per_step))
+        del scratch
+    else:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            run()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+        ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
     wall = time.perf_counter() - t0
-    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
-    ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} steps{' (cold)' if args.cold else ''}: "
+          f"{ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
     # the first pass alone, as the step launches it: the planned decode on a plan computed
-    # beforehand is that single launch (split sequences are merged inside it)
+    # beforehand is that single launch when split sequences are merged inside it; past
+    # the library's in-pass limit the combine is a launch of its own, and the first pass
+    # is timed without it
     plan_ws = pkv.decode_plan(ctx, tables, hq, d, max_ctx, P)
+    np_max = max(1, -(-max_ctx // P)) if P > 0 else 1
     timed_kernel = "decode_pass1_kernel"
     if shared_path:
         # no single dominant kernel: the whole decode call (plan, shared-prefix pass, first
@@ -501,6 +533,14 @@ def main():
 
         def pass1():
             shared_decode(0)
+    elif np_max > pkv.IN_PASS_MERGE_MAX_PARTITIONS:
+        part_out = torch.empty((B, hq, np_max, d), dtype=torch.float32, device="cuda")
+        part_lse = torch.empty((B, hq, np_max), dtype=torch.float32, device="cuda")
+
+        def pass1():
+            pkv.paged_decode_partials(q, kc, vc, tables, ctx, max_ctx, P, scale=scale,
+                                      part_out=part_out, part_lse=part_lse,
+                                      plan_workspace=plan_ws)
     else:
         def pass1():
             pkv.paged_decode_planned(q, kc, vc, tables, ctx, max_ctx, plan_ws, scale=scale,
@@ -509,13 +549,27 @@ def main():
     for _ in range(5):
         pass1()
     torch.cuda.synchronize()
-    ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ks.record(stream)
-    for _ in range(args.kernel_reps):
-        pass1()
-    ke.record(stream)
-    torch.cuda.synchronize()
-    pass1_s = ks.elapsed_time(ke) / 1e3 / args.kernel_reps
+    if args.cold:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        marks = []
+        for i in range(args.kernel_reps):
+            scratch.fill_(i & 0xFF)
+            ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ks.record(stream)
+            pass1()
+            ke.record(stream)
+            marks.append((ks, ke))
+        torch.cuda.synchronize()
+        pass1_s = float(np.mean([ks.elapsed_time(ke) for ks, ke in marks])) / 1e3
+        del scratch
+    else:
+        ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ks.record(stream)
+        for _ in range(args.kernel_reps):
+            pass1()
+        ke.record(stream)
+        torch.cuda.synchronize()
+        pass1_s = ks.elapsed_time(ke) / 1e3 / args.kernel_reps
     flags = pkv.device_error()
     if flags:
         raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
@@ -530,9 +584,7 @@ def main():
     step_bytes = layers * (p1_bytes + append_bytes)
     value = step_bytes / step_s / 1e9
     achieved = p1_bytes / pass1_s / 1e9
-    # the counters were taken on the seed-0 instance of this workload only
-    traffic = (traffic_from_profile()
-               if args.workload == "high_concurrency" and P == 4096 and args.seed == 0 else None)
+    traffic = traffic_from_profile(args.workload, P, args.seed)
 
     probe = None if args.no_copy_probe else copy_probe(torch)
 
@@ -572,9 +624,14 @@ def main():
                      "launch), LSE combine"
                      if shared_path else
                      "append 1 token/seq + work plan (one launch), split-KV first pass with "
-                     "the LSE merge of split sequences in the same launch"),
+                     "the LSE merge of split sequences in the same launch"
+                     if np_max <= pkv.IN_PASS_MERGE_MAX_PARTITIONS else
+                     "append 1 token/seq + work plan (one launch), split-KV first pass, "
+                     "LSE combine (one launch)"),
             "appended_tokens_per_layer": total_new,
             "launch": "hip graph of the whole step" if args.graph else "eager",
+            "caches": ("cold: 1 GiB written before every step" if args.cold
+                       else "warm: steps back to back"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_ctx / step_s, 1),

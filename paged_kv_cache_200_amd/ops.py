@@ -17,6 +17,9 @@ import torch
 from . import _lib
 
 BLOCK_SIZE = 16
+# pkv_paged_decode merges a split sequence inside its first pass up to this many
+# partitions, and in a second (combine) launch past it (include/pkv.h)
+IN_PASS_MERGE_MAX_PARTITIONS = 8
 _BF16_TYPES = (torch.bfloat16, torch.uint16, torch.int16)
 
 

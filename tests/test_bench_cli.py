@@ -25,5 +25,6 @@ def test_defaults():
         a = bench.parse_args()
     finally:
         sys.argv = old
-    assert (a.gpus, a.workload, a.partition_size, a.graph) == (1, "high_concurrency", None, False)
+    assert (a.gpus, a.workload, a.partition_size, a.graph, a.cold) == (1, "high_concurrency",
+                                                                       None, False, False)
     assert a.steps * 0.25e-3 < 60   # the default timed region stays well under a minute
