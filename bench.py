@@ -70,6 +70,12 @@ def parse_args():
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="decode fork workloads with the plain path (each fork re-reads the "
                         "shared prefix) instead of the shared-prefix path")
+    p.add_argument("--append-in-pass", choices=["auto", "yes", "no"], default="auto",
+                   help="plain decode: one work plan per step, then one launch per layer that "
+                        "appends the new tokens and attends (pkv_append_paged_decode_planned), "
+                        "instead of a plan + append launch and a first-pass launch per layer; "
+                        "auto: when the step has more than one layer (measured faster there, "
+                        "3 us slower on one layer)")
     p.add_argument("--cold", action="store_true",
                    help="write a 1 GiB scratch buffer before every timed step (outside the "
                         "timed region), so no step finds the previous one's data in the L2 "
@@ -436,7 +442,20 @@ def main():
                                        max_shared, max_ctx, scale=scale, partition_size=P,
                                        out=out, lse=lse, workspace=ws)
 
+    in_pass = not shared_path and (args.append_in_pass == "yes" or
+                                   (args.append_in_pass == "auto" and layers > 1))
+    if in_pass:
+        step_plan = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
     def step():
+        if in_pass:
+            # lengths advance once per step, so one plan serves every layer
+            pkv.decode_plan(ctx, tables, hq, d, max_ctx, P, workspace=step_plan)
+            for l in range(layers):
+                pkv.append_paged_decode_planned(qs[l], kcs[l], vcs[l], k_new, v_new, tables,
+                                                start, cu, ctx, max_ctx, step_plan, scale=scale,
+                                                partition_size=P, out=out, lse=lse)
+            return
         for l in range(layers):
             if shared_path:
                 # fork groups: append and work plan in one launch, then one decode launch
@@ -623,6 +642,11 @@ def main():
             "step": ("append + work plan (one launch), shared-prefix and private ranges (one "
                      "launch), LSE combine"
                      if shared_path else
+                     "work plan (one launch per step), then per layer one launch that appends "
+                     "1 token/seq and runs the split-KV first pass with the LSE merge"
+                     + ("" if np_max <= pkv.IN_PASS_MERGE_MAX_PARTITIONS
+                        else ", then the LSE combine (one launch)")
+                     if in_pass else
                      "append 1 token/seq + work plan (one launch), split-KV first pass with "
                      "the LSE merge of split sequences in the same launch"
                      if np_max <= pkv.IN_PASS_MERGE_MAX_PARTITIONS else

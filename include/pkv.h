@@ -203,6 +203,32 @@ int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache
                             int32_t dtype, pkv_stream_t stream);
 
 /*
+ * One decode step of one layer in one launch, on a plan made beforehand: exactly
+ * pkv_kv_append(...) followed by pkv_paged_decode_planned(...) with the same arguments,
+ * results and errors.  The plan must come from pkv_decode_plan on the same stream, into
+ * the same workspace, for the same context_lens contents, batch, max_context_len and
+ * partition_size; one plan serves every layer of a step (lengths advance once per step,
+ * spindle, "Two bugs worth recording").  The first pass writes the new tokens itself:
+ * sequence s's token i (row cu_new_tokens[s] + i of k_new / v_new, [total_new,
+ * num_kv_heads, head_dim]) goes to position start_pos[s] + i, explicit, never inferred;
+ * the workgroup whose token range holds that position stores it before streaming, and
+ * a position past context_lens[s] is stored by the sequence's last workgroup.  Device
+ * errors (bad cu_new_tokens, positions outside the table row, block ids outside the pool)
+ * set the same bits as pkv_kv_append.  Past 8 partitions per sequence the combine
+ * follows as a second launch.
+ */
+int pkv_append_paged_decode_planned(float* out, float* lse, const void* q, void* k_cache,
+                                    void* v_cache, const void* k_new, const void* v_new,
+                                    const int32_t* block_tables, int64_t bt_stride,
+                                    const int32_t* start_pos, const int32_t* cu_new_tokens,
+                                    int32_t total_new, const int32_t* context_lens,
+                                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_context_len, float scale,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+
+/*
  * Decode for a batch holding copy-on-write fork groups (spindle, "Paging":
  * forked sequences share blocks through reference counts).  Computes the
  * same out and lse as pkv_paged_decode (equal within rounding; the shared

@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     BLOCK_SIZE,
     IN_PASS_MERGE_MAX_PARTITIONS,
     append_paged_decode,
+    append_paged_decode_planned,
     append_paged_decode_shared_prefix,
     copy_blocks,
     decode_plan,

@@ -175,6 +175,74 @@ constexpr int kSlotMask = kDirectFlag - 1;
 // Workgroups per compute unit the register allocation is held to: two (eight waves, at
 // most 256 registers per lane) where that fits without spilling, measured per shape with
 // the compiler's resource report; the other shapes take what their registers allow.
+// A decode step's KV append folded into the first pass (spindle, "Two bugs worth
+// recording": append writes at an explicit start position).  Sequence s's new tokens,
+// rows cu[s] .. cu[s + 1] - 1 of k_new / v_new at positions start_pos[s] + i, are written
+// by the unit whose token range holds their position, or by the sequence's last unit when
+// the position lies past the attended range.  Inside that unit each 16-byte chunk is
+// stored by the lane of the wave that later loads it as part of its block (same lane,
+// same address), so the attention reads the new token without a barrier: a thread always
+// sees its own earlier write.  Errors are flagged like the standalone append's.
+struct PassAppend {
+  const void* k_new;  // [total][num_kv_heads][head_dim], nullptr: nothing to append
+  const void* v_new;
+  const int32_t* start_pos;
+  const int32_t* cu;
+  int total;
+};
+
+template <typename T, int D, int NW>
+__device__ __forceinline__ void append_in_unit(
+    T* kc, T* vc, const PassAppend& ap, const int32_t* __restrict__ tables, int W,
+    const int32_t* __restrict__ ctx_lens, int s, int kvh, int num_kv_heads, int num_blocks,
+    int tok0, int tok1, int wave, int lane) {
+  using Gm = Geom<T, D>;
+  const int c0 = ap.cu[s];
+  const int c1 = ap.cu[s + 1];
+  if (c0 < 0 || c1 < c0 || c1 > ap.total) {
+    if (wave == 0 && lane == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CU);
+    return;
+  }
+  const int cap = W * kBlockTokens;
+  int n = ctx_lens[s];
+  n = n < 0 ? 0 : min(n, cap);
+  const bool last_unit = tok1 >= n;
+  const int p0 = ap.start_pos[s];
+  const int b_begin = tok0 / kBlockTokens;
+  const int grp = lane / kLanesPerToken;
+  const int sub = lane % kLanesPerToken;
+  const T* kn = static_cast<const T*>(ap.k_new);
+  const T* vn = static_cast<const T*>(ap.v_new);
+  for (int t = c0; t < c1; ++t) {
+    const int pos = p0 + (t - c0);
+    const bool inside = pos >= tok0 && pos < tok1;
+    if (!inside && !(last_unit && pos >= tok1)) continue;
+    if (pos < 0 || pos >= cap) {
+      if (wave == 0 && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_POSITION);
+      continue;
+    }
+    const int bi = pos / kBlockTokens;
+    // the unit's blocks go round-robin over its waves from b_begin
+    const int owner = inside ? (bi - b_begin) % NW : 0;
+    const int slot = pos % kBlockTokens;
+    // lanes of token group slot % 8 hold slot as their token slot / 8 of the block
+    if (wave != owner || grp != slot % kGroups) continue;
+    const int id = tables[static_cast<size_t>(s) * W + bi];
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks)) {
+      if (sub == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+      continue;
+    }
+    const size_t row = ((static_cast<size_t>(id) * num_kv_heads + kvh) * kBlockTokens + slot) * D;
+    const size_t src = (static_cast<size_t>(t) * num_kv_heads + kvh) * D;
+#pragma unroll
+    for (int c = 0; c < Gm::kChunks; ++c) {
+      const int e = sub * Gm::kChunkElems + c * Gm::kChunkStride;
+      *reinterpret_cast<uint4*>(kc + row + e) = *reinterpret_cast<const uint4*>(kn + src + e);
+      *reinterpret_cast<uint4*>(vc + row + e) = *reinterpret_cast<const uint4*>(vn + src + e);
+    }
+  }
+}
+
 template <typename T, int D, int G>
 constexpr int pass1_min_workgroups() {
   constexpr int max_g = sizeof(T) == 2 ? (D == 64 ? 7 : 4) : (D == 64 ? 5 : 2);
@@ -189,7 +257,7 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
     int max_parts, float* __restrict__ part_out, float* __restrict__ part_lse,
     float* __restrict__ out, float* __restrict__ lse, int order,
     const int4* __restrict__ plan, const int* __restrict__ plan_count,
-    const int32_t* __restrict__ nslots, int* __restrict__ merge_ctr) {
+    const int32_t* __restrict__ nslots, int* __restrict__ merge_ctr, const PassAppend ap) {
   using Gm = Geom<T, D>;
   int part, kvh, s;  // part: the partial-result slot written unless `direct`
   int tok0, tok1;    // the unit's token range
@@ -237,6 +305,10 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
   }
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
+  // (unlikely and out of line, so the block loop's registers are those of plain decode)
+  if (__builtin_expect(ap.k_new != nullptr, 0))
+    append_in_unit<T, D, NW>(const_cast<T*>(kc), const_cast<T*>(vc), ap, tables, W, ctx_lens, s,
+                             kvh, num_kv_heads, num_blocks, tok0, tok1, wave, lane);
 
   GroupState<T, D, G> st;
   attend_range<T, D, G, NW, true>(st, q, kc, vc, tables, W, s, s, kvh, num_q_heads,
@@ -761,7 +833,7 @@ __global__ __launch_bounds__(kTileWaves * kWave) void decode_shared_mfma_kernel(
 using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
                           const int32_t*, int, const int32_t*, int, int, int, float, int, int,
                           float*, float*, float*, float*, const int4*, const int*,
-                          const int32_t*, int*);
+                          const int32_t*, int*, const PassAppend&);
 
 // order = kOrderPlanned: plan/plan_count from plan_kernel, grid of batch * np units.
 template <int NW, typename T, int D, int G>
@@ -770,7 +842,7 @@ void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t st
                   const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                   int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
                   float* lse, const int4* plan, const int* plan_count, const int32_t* nslots,
-                  int* merge_ctr) {
+                  int* merge_ctr, const PassAppend& ap) {
   static_assert(NW > 1, "split sequences are merged in the multi-wave epilogue");
   dim3 grid;
   if (order == kOrderPlanned)
@@ -783,7 +855,7 @@ void pass1_launch(int order, int np, int num_kv_heads, int batch, hipStream_t st
                      stream, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
                      part_tokens, max_parts, part_out, part_lse, out, lse, order, plan,
-                     plan_count, nslots, merge_ctr);
+                     plan_count, nslots, merge_ctr, ap);
 }
 
 // The configuration the library ships: four waves share a (sequence, KV head,
@@ -794,10 +866,10 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
                    const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
                    int part_tokens, int max_parts, float* part_out, float* part_lse, float* out,
                    float* lse, const int4* plan, const int* plan_count, const int32_t* nslots,
-                   int* merge_ctr) {
+                   int* merge_ctr, const PassAppend& ap) {
   pass1_launch<4, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx, hq,
                            hkv, nb, scale_log2, part_tokens, max_parts, part_out, part_lse, out,
-                           lse, plan, plan_count, nslots, merge_ctr);
+                           lse, plan, plan_count, nslots, merge_ctr, ap);
 }
 
 struct SharedArgs {
@@ -1026,7 +1098,8 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                 size_t workspace_bytes, int32_t dtype, pkv_stream_t stream,
-                const AppendArgs* append = nullptr, const Groups* groups = nullptr) {
+                const AppendArgs* append = nullptr, const Groups* groups = nullptr,
+                bool append_in_pass = false) {
   LaunchFn fn = nullptr;
   int st = check_decode_args(q, k_cache, v_cache, block_tables, bt_stride, context_lens, batch,
                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -1054,7 +1127,14 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
                                   shared ? groups->max_shared_blocks : 0,
                                   in_pass_merge ? w.merge_ctr : nullptr,
                                   in_pass_merge ? batch * num_q_heads : 0);
-  if (append != nullptr && append->total > 0) {
+  // The append runs inside the first pass (plan made beforehand), or beside the plan in
+  // one prologue launch, or on its own.
+  PassAppend pa{nullptr, nullptr, nullptr, nullptr, 0};
+  if (append_in_pass) {
+    if (shared || make_plan) return PKV_ERR_ARG;
+    if (append != nullptr && append->total > 0)
+      pa = PassAppend{append->k_new, append->v_new, append->start_pos, append->cu, append->total};
+  } else if (append != nullptr && append->total > 0) {
     const int eb = elem_bytes(dtype);
     const int wgs = 1 + (append->total + kAppendPerGroup - 1) / kAppendPerGroup;
     hipLaunchKernelGGL(prologue_kernel, dim3(wgs), dim3(kPlanThreads), 0, s, w.plan,
@@ -1098,7 +1178,7 @@ int decode_impl(bool make_plan, float* out, float* lse, const void* q, const voi
     fn(kOrderPlanned, geo.max_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
        static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
        scale_log2, geo.tokens, geo.max_slots, w.part_out, w.part_lse, out, lse, w.plan,
-       w.plan_count, w.nslots, in_pass_merge ? w.merge_ctr : nullptr);
+       w.plan_count, w.nslots, in_pass_merge ? w.merge_ctr : nullptr, pa);
     if ((st = launch_status()) != PKV_OK) return st;
   }
   if (geo.partials && !in_pass_merge) {
@@ -1230,6 +1310,22 @@ extern "C" int pkv_append_paged_decode(
                      stream, &a);
 }
 
+extern "C" int pkv_append_paged_decode_planned(
+    float* out, float* lse, const void* q, void* k_cache, void* v_cache, const void* k_new,
+    const void* v_new, const int32_t* block_tables, int64_t bt_stride, const int32_t* start_pos,
+    const int32_t* cu_new_tokens, int32_t total_new, const int32_t* context_lens, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
+    void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+  AppendArgs a;
+  const int st = make_append(k_new, v_new, start_pos, cu_new_tokens, total_new, &a);
+  if (st != PKV_OK) return st;
+  return decode_impl(false, out, lse, q, k_cache, v_cache, block_tables, bt_stride,
+                     context_lens, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream, &a, nullptr, true);
+}
+
 extern "C" int pkv_paged_decode_shared_prefix(
     float* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
@@ -1310,7 +1406,7 @@ extern "C" int pkv_paged_decode_partials(float* part_out, float* part_lse, const
   fn(order, grid_slots, num_kv_heads, batch, s, q, k_cache, v_cache, block_tables,
      static_cast<int>(bt_stride), context_lens, num_q_heads, num_kv_heads, num_blocks,
      scale_to_log2(scale), partition_size, max_partitions, part_out, part_lse, nullptr, nullptr,
-     plan, plan_count, nullptr, nullptr);
+     plan, plan_count, nullptr, nullptr, PassAppend{nullptr, nullptr, nullptr, nullptr, 0});
   return launch_status();
 }
 

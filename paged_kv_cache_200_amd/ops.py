@@ -243,6 +243,33 @@ def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_p
     return out, lse
 
 
+def append_paged_decode_planned(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
+                                cu_new_tokens, context_lens, max_context_len, workspace,
+                                scale=None, partition_size=0, out=None, lse=None,
+                                want_lse=True, stream=None):
+    """kv_append then paged_decode in one launch, on a plan that decode_plan wrote into
+    `workspace` for the same context_lens (one plan serves every layer of a step).
+
+    context_lens must already count the appended tokens.
+    """
+    if workspace is None:
+        raise ValueError("append_paged_decode_planned needs the workspace decode_plan filled")
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+    need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
+    workspace, wbytes = _workspace(workspace, need, q.device)
+    _lib.call("pkv_append_paged_decode_planned", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
+              _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+              block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
+              _ptr(context_lens), B, hq, hkv, d, BLOCK_SIZE, nb, int(max_context_len),
+              float(scale), int(partition_size), _ptr(workspace), wbytes, _kv_code(k_cache),
+              _stream(stream))
+    return out, lse
+
+
 def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_starts,
                                group_shared_blocks, max_shared_blocks, max_context_len,
                                scale=None, partition_size=0, out=None, lse=None, workspace=None,

@@ -27,4 +27,5 @@ def test_defaults():
         sys.argv = old
     assert (a.gpus, a.workload, a.partition_size, a.graph, a.cold) == (1, "high_concurrency",
                                                                        None, False, False)
+    assert a.append_in_pass == "auto"
     assert a.steps * 0.25e-3 < 60   # the default timed region stays well under a minute

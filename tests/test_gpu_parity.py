@@ -517,3 +517,96 @@ def test_in_pass_merge_sees_this_calls_partials(wl, P):
             assert_parity((o.cpu().numpy(), l.cpu().numpy()), oracle_decode(case, q=qh),
                           case.kv_dtype, f"{wl} P{P}")
     assert_no_device_error()
+
+
+@pytest.mark.parametrize("P", [0, 512, 4096])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_append_in_pass_equals_separate_calls(P, kv_dtype):
+    """pkv_append_paged_decode_planned (the append written by the first pass itself) equals
+    kv_append followed by paged_decode_planned, bit for bit (outputs and pools), for new
+    tokens at the first and last slot of a block, at a partition's first token, in the
+    middle of the attended range, past it, several per sequence and none; and the oracle
+    within tolerance."""
+    hkv, hq, d = (8, 32, 128) if kv_dtype == "bf16" else (12, 12, 64)
+    lens = [1, 16, 17, 4097, 700, 512, 5000, 33, 64]
+    case = build_case("step_in_pass", lens, hq, hkv, d, kv_dtype, seed=P + d + 1)
+    B = case.batch
+    # (start, count) per sequence: the last token, a whole last block, a partition's first
+    # token, two tokens in the middle, none, one past the attended range
+    spec = [(0, 1), (15, 1), (16, 1), (4096, 1), (698, 2), (0, 0), (4990, 3), (33, 1),
+            (63, 1)]
+    start = np.array([p for p, _ in spec], np.int32)
+    counts = [c for _, c in spec]
+    cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(cu[-1])
+    rng = np.random.default_rng(P + 7)
+    kn = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    if kv_dtype == "bf16":
+        kn, vn = bf16_bits(kn), bf16_bits(vn)
+    ops = _ops()
+    a, b = DeviceCase(case), DeviceCase(case)
+    ws_a = ops.decode_plan(a.ctx, a.tables, hq, d, a.max_ctx, P)
+    ws_b = ops.decode_plan(b.ctx, b.tables, hq, d, b.max_ctx, P)
+    say(f"  append in pass {kv_dtype} P{P}")
+    o1, l1 = ops.append_paged_decode_planned(a.q, a.k, a.v, dev(kn), dev(vn), a.tables,
+                                             dev(start), dev(cu), a.ctx, a.max_ctx, ws_a,
+                                             scale=float(case.scale), partition_size=P)
+    ops.kv_append(b.k, b.v, dev(kn), dev(vn), b.tables, dev(start), dev(cu))
+    o2, l2 = ops.paged_decode_planned(b.q, b.k, b.v, b.tables, b.ctx, b.max_ctx, ws_b,
+                                      scale=float(case.scale), partition_size=P)
+    torch.cuda.synchronize()
+    assert a.k.cpu().numpy().tobytes() == b.k.cpu().numpy().tobytes()
+    assert a.v.cpu().numpy().tobytes() == b.v.cpu().numpy().tobytes()
+    assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes()
+    assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes()
+    kp, vp = pa.kv_append(case.k_pool[0], case.v_pool[0], kn, vn, case.block_tables, start, cu)
+    want = pa.paged_decode(case.q[0], kp, vp, case.block_tables, case.context_lens, case.scale,
+                           kv_dtype)
+    assert_parity((o1.cpu().numpy(), l1.cpu().numpy()), want, kv_dtype, f"append in pass P{P}")
+    assert_no_device_error()
+
+
+def test_append_in_pass_over_layers_with_one_plan():
+    """One plan per step, one launch per layer: every layer's pool and output equal the
+    separate calls', and a position outside the table row is flagged like kv_append's."""
+    case = config_case("qwen_gqa", 2, layers=3, max_batch=24)
+    ops = _ops()
+    si_start = (case.context_lens - 1).astype(np.int32)
+    cu = np.arange(case.batch + 1, dtype=np.int32)
+    rng = np.random.default_rng(11)
+    P = 256
+    plan = None
+    for layer in range(3):
+        kn = bf16_bits(rng.standard_normal((case.batch, case.num_kv_heads, case.head_dim))
+                       .astype(np.float32))
+        vn = bf16_bits(rng.standard_normal((case.batch, case.num_kv_heads, case.head_dim))
+                       .astype(np.float32))
+        a, b = DeviceCase(case, layer), DeviceCase(case, layer)
+        if plan is None:
+            plan = ops.decode_plan(a.ctx, a.tables, case.num_q_heads, case.head_dim, a.max_ctx, P)
+        o1, l1 = ops.append_paged_decode_planned(a.q, a.k, a.v, dev(kn), dev(vn), a.tables,
+                                                 dev(si_start), dev(cu), a.ctx, a.max_ctx, plan,
+                                                 scale=float(case.scale), partition_size=P)
+        o2, l2 = ops.append_paged_decode(b.q, b.k, b.v, dev(kn), dev(vn), b.tables,
+                                         dev(si_start), dev(cu), b.ctx, b.max_ctx,
+                                         scale=float(case.scale), partition_size=P)
+        torch.cuda.synchronize()
+        assert a.k.cpu().numpy().tobytes() == b.k.cpu().numpy().tobytes(), layer
+        assert a.v.cpu().numpy().tobytes() == b.v.cpu().numpy().tobytes(), layer
+        assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes(), layer
+        assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes(), layer
+    assert_no_device_error()
+    # a position one past the table row: nothing is written, the position bit is set
+    dc = DeviceCase(case)
+    bad = si_start.copy()
+    bad[3] = case.block_tables.shape[1] * 16
+    before = dc.k.cpu().numpy().tobytes()
+    ops.append_paged_decode_planned(dc.q, dc.k, dc.v, dev(kn), dev(vn), dc.tables, dev(bad),
+                                    dev(cu), dc.ctx, dc.max_ctx, plan, scale=float(case.scale),
+                                    partition_size=P)
+    torch.cuda.synchronize()
+    flags = ops.device_error()
+    assert flags & 2, flags
+    after = dc.k.cpu().numpy()
+    assert after.tobytes() != before  # the other sequences' tokens were written
