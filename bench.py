@@ -41,9 +41,14 @@ DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
 
 
 def decode_source_digest():
+    """SHA-256 of the first pass's code: its sources without // comments, trailing blanks
+    and empty lines, so that editing a comment keeps the counters taken on that code."""
     h = hashlib.sha256()
     for path in DECODE_SRCS:
-        h.update(open(path, "rb").read())
+        for line in open(path, encoding="utf-8").read().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -212,7 +212,9 @@ int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache
  * sequence s's token i (row cu_new_tokens[s] + i of k_new / v_new, [total_new,
  * num_kv_heads, head_dim]) goes to position start_pos[s] + i, explicit, never inferred;
  * the workgroup whose token range holds that position stores it before streaming, and
- * a position past context_lens[s] is stored by the sequence's last workgroup.  Device
+ * a position past context_lens[s] is stored by the sequence's last workgroup.  No other
+ * sequence of the call may attend an appended slot (copy-on-write: a block held by
+ * several sequences is copied with pkv_copy_blocks before it is written).  Device
  * errors (bad cu_new_tokens, positions outside the table row, block ids outside the pool)
  * set the same bits as pkv_kv_append.  Past 8 partitions per sequence the combine
  * follows as a second launch.

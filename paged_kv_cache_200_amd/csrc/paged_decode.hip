@@ -182,7 +182,9 @@ constexpr int kSlotMask = kDirectFlag - 1;
 // the position lies past the attended range.  Inside that unit each 16-byte chunk is
 // stored by the lane of the wave that later loads it as part of its block (same lane,
 // same address), so the attention reads the new token without a barrier: a thread always
-// sees its own earlier write.  Errors are flagged like the standalone append's.
+// sees its own earlier write.  No other workgroup may read the written slot in the same
+// launch, which copy-on-write guarantees (a block held by several sequences is copied
+// before any of them writes into it).  Errors are flagged like the standalone append's.
 struct PassAppend {
   const void* k_new;  // [total][num_kv_heads][head_dim], nullptr: nothing to append
   const void* v_new;
@@ -305,7 +307,8 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
   }
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  // (unlikely and out of line, so the block loop's registers are those of plain decode)
+  // (marked unlikely, which keeps the block loop's register allocation that of plain
+  // decode)
   if (__builtin_expect(ap.k_new != nullptr, 0))
     append_in_unit<T, D, NW>(const_cast<T*>(kc), const_cast<T*>(vc), ap, tables, W, ctx_lens, s,
                              kvh, num_kv_heads, num_blocks, tok0, tok1, wave, lane);
