@@ -82,7 +82,7 @@ def parse_args():
                         "auto: when the step has more than one layer (measured faster there, "
                         "3 us slower on one layer)")
     p.add_argument("--cold", action="store_true",
-                   help="write a 1 GiB scratch buffer before every timed step (outside the "
+                   help="read a 1 GiB scratch buffer before every timed step (outside the "
                         "timed region), so no step finds the previous one's data in the L2 "
                         "or the 256 MB Infinity Cache; each step is then timed on its own")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -514,12 +514,13 @@ def main():
     t0 = time.perf_counter()
     if args.cold:
         # every step on its own, after a 1 GiB write that evicts L2 and Infinity Cache
-        # (no host synchronisation between steps: while the GPU writes the scratch buffer
-        # the host enqueues the step, so no step waits for its own launches)
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # The sweep reads: a written sweep would leave the Infinity Cache full of dirty
+        # lines, and a step whose loads allocate there would pay their write-back.  (No host
+        # synchronisation between steps: while the GPU sweeps, the host enqueues the step.)
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         marks = []
         for i in range(args.steps):
-            scratch.fill_(i & 0xFF)
+            scratch.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             run()
@@ -574,10 +575,10 @@ def main():
         pass1()
     torch.cuda.synchronize()
     if args.cold:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         marks = []
         for i in range(args.kernel_reps):
-            scratch.fill_(i & 0xFF)
+            scratch.sum()
             ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ks.record(stream)
             pass1()
@@ -659,7 +660,7 @@ def main():
                      "LSE combine (one launch)"),
             "appended_tokens_per_layer": total_new,
             "launch": "hip graph of the whole step" if args.graph else "eager",
-            "caches": ("cold: 1 GiB written before every step" if args.cold
+            "caches": ("cold: 1 GiB read before every step" if args.cold
                        else "warm: steps back to back"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
