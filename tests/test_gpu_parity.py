@@ -407,6 +407,26 @@ def test_plan_lists_every_unit_once_in_order(P):
 @pytest.mark.parametrize("P", [64, 512, 2048])
 def test_decode_equals_partials_plus_combine_bitwise(P):
     case = config_case("high_concurrency", 0)
+    _check_decode_equals_partials_plus_combine(case, P)
+
+
+@pytest.mark.parametrize("kv_dtype,hq,hkv,d,lens,P", [
+    ("bf16", 14, 2, 64, [2297, 1, 512, 513, 1800, 40], 512),   # Qwen shape, up to 5 slots
+    ("f32", 12, 12, 64, [192, 17, 100, 64], 32),                # 6 slots
+    ("f32", 8, 2, 128, [700, 5, 256, 129], 128),                # 6 slots
+    ("bf16", 32, 8, 128, [1024, 1023, 897, 9, 600], 128),       # 8 slots: the in-pass limit
+    ("bf16", 32, 8, 128, [1152, 1151, 1025, 9, 600], 128),      # 9 slots: the combine launch
+])
+def test_decode_equals_partials_plus_combine_shapes(kv_dtype, hq, hkv, d, lens, P):
+    """The merge of split sequences, inside the first pass up to 8 partitions and in the
+    combine kernel past that, equals the first pass's partials + the standalone combine,
+    bit for bit, for every head shape it is compiled for here."""
+    case = build_case("merge", lens, hq, hkv, d, kv_dtype, seed=len(lens) + P)
+    _check_decode_equals_partials_plus_combine(case, P)
+    assert_parity(run_decode(DeviceCase(case), P), oracle_decode(case), kv_dtype, f"merge P{P}")
+
+
+def _check_decode_equals_partials_plus_combine(case, P):
     dc = DeviceCase(case)
     ops = _ops()
     fo, fl = ops.paged_decode(dc.q, dc.k, dc.v, dc.tables, dc.ctx, dc.max_ctx,
