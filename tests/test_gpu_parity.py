@@ -548,13 +548,14 @@ def test_append_in_pass_equals_separate_calls(P, kv_dtype):
     middle of the attended range, past it, several per sequence and none; and the oracle
     within tolerance."""
     hkv, hq, d = (8, 32, 128) if kv_dtype == "bf16" else (12, 12, 64)
-    lens = [1, 16, 17, 4097, 700, 512, 5000, 33, 64]
+    lens = [1, 16, 17, 4097, 700, 512, 5000, 33, 64, 0, 60]
     case = build_case("step_in_pass", lens, hq, hkv, d, kv_dtype, seed=P + d + 1)
     B = case.batch
     # (start, count) per sequence: the last token, a whole last block, a partition's first
-    # token, two tokens in the middle, none, one past the attended range
+    # token, two tokens in the middle, none, one past the attended range, one into an empty
+    # context, twenty across a block boundary
     spec = [(0, 1), (15, 1), (16, 1), (4096, 1), (698, 2), (0, 0), (4990, 3), (33, 1),
-            (63, 1)]
+            (63, 1), (0, 1), (40, 20)]
     start = np.array([p for p, _ in spec], np.int32)
     counts = [c for _, c in spec]
     cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
