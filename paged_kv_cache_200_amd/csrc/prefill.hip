@@ -68,9 +68,11 @@ constexpr int kLdsThreads = kLdsWaves * kWave;
 
 template <int D>
 struct LdsStage {
-  static constexpr int kRowElems = D + 8;  // 16-byte pad per token row
+  static constexpr int kRowElems = D + 8;    // K rows: 16-byte pad per token row
+  static constexpr int kVRowElems = D + 16;  // V rows: 32-byte pad (the transpose reads below
+                                             // then touch each bank window once per pass)
   alignas(16) uint16_t k[kBlockTokens * kRowElems];
-  alignas(16) uint16_t v[kBlockTokens * kRowElems];
+  alignas(16) uint16_t v[kBlockTokens * kVRowElems];
 };
 
 template <int D>
@@ -102,31 +104,118 @@ __device__ __forceinline__ void stage_store(LdsStage<D>& st, const StageRegs<D>&
     const int i = tid + j * kLdsThreads;
     const int ii = i < kHalf ? i : i - kHalf;
     uint16_t* dst = (i < kHalf ? st.k : st.v) +
-                    (ii / kRowChunks) * LdsStage<D>::kRowElems + (ii % kRowChunks) * 8;
+                    (ii / kRowChunks) * (i < kHalf ? LdsStage<D>::kRowElems
+                                                   : LdsStage<D>::kVRowElems) +
+                    (ii % kRowChunks) * 8;
     *reinterpret_cast<u32x4_t*>(dst) = r.w[j];
   }
 }
 
-// The lane's MFMA operands of a staged block (same layouts as mfma_load_block).
+// The lane's MFMA operands of a staged block.  K as in mfma_load_block.  V through the
+// gfx950 LDS transpose read: within each 16-lane group, ds_read_b64_tr_b16 gives lane i
+// element i % 4 of the 8-byte chunks addressed by lanes i / 4 + 4k (k = 0..3), so lane
+// (c, h) addressing V[4h + c / 4][16j + 4 (c % 4)] receives V[4h .. 4h + 3][16j + c]: the
+// B operand of output tile j (dims 16j .. 16j + 15, lane c holding dim 16j + c), with no
+// repacking on the VALU.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
 template <int D>
-__device__ __forceinline__ void stage_read(MfmaBlock<D>& b, const LdsStage<D>& st, int c, int h) {
+struct TrBlock {
+  u32x4_t k[MfmaGeom<D>::kQkSteps];
+  u32x2_t vt[MfmaGeom<D>::kTiles];  // tile j: V[4h .. 4h + 3][16j + c], two tokens a word
+};
+
+template <int D>
+__device__ __forceinline__ void stage_read_tr(TrBlock<D>& b, const LdsStage<D>& st, int c,
+                                              int h) {
   using Mg = MfmaGeom<D>;
   constexpr int RS = LdsStage<D>::kRowElems;
+  constexpr int RV = LdsStage<D>::kVRowElems;
 #pragma unroll
   for (int k = 0; k < Mg::kQkSteps; ++k)
     b.k[k] = *reinterpret_cast<const u32x4_t*>(st.k + c * RS + 32 * k + 8 * h);
+  const uint16_t* vrow = st.v + (4 * h + c / 4) * RV + 4 * (c % 4);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint16_t* src = st.v + (4 * h + k) * RS + c * Mg::kTiles;
-    if constexpr (Mg::kVWords == 4) {
-      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
+  for (int j = 0; j < Mg::kTiles; ++j) {
+    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)(vrow + 16 * j));
+    b.vt[j] = __builtin_bit_cast(u32x2_t, t);
+  }
+}
+
+// mfma_rows_block on a transpose-read block: the same scores, softmax and two-term P, with
+// output tile j holding dims 16j + c.
+template <int D>
+__device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
+                                              const u32x4_t (&qr)[MfmaGeom<D>::kQkSteps],
+                                              int t_base, int n_c, int n_max, int h,
+                                              float scale_log2) {
+  using Mg = MfmaGeom<D>;
+  f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b.v[k][j] = w[j];
-    } else {
-      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
-      b.v[k][0] = w[0];
-      b.v[k][1] = w[1];
+  for (int s = 0; s < Mg::kQkSteps; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
+                                                 __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
+                                                 0);
+  float x[4];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
+    bm = fmaxf(bm, x[i]);
+  }
+  bm = max_xor32(max_xor16(bm));
+  const bool raise = bm > r.m_c + kLazyMaxSlack;
+  if (__any(raise)) {
+    float a = 1.0f;
+    if (raise) {
+      a = r.m_c == -INFINITY ? 0.0f : fast_exp2(r.m_c - bm);
+      r.m_c = bm;
     }
+    r.l_part *= a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(a, 4 * h + i);
+#pragma unroll
+      for (int j = 0; j < Mg::kTiles; ++j) r.o[j][i] *= ai;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - r.m_c);
+    r.l_part += p[i];
+  }
+  uint32_t pw[4], rw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pw[i] = __float_as_uint(p[i]);
+    rw[i] = __float_as_uint(p[i] - __uint_as_float(pw[i] & 0xffff0000u));
+  }
+  const bf16x8_t a = __builtin_bit_cast(
+      bf16x8_t, u32x4_t{__builtin_amdgcn_perm(pw[1], pw[0], kHighHalves),
+                        __builtin_amdgcn_perm(pw[3], pw[2], kHighHalves),
+                        __builtin_amdgcn_perm(rw[1], rw[0], kHighHalves),
+                        __builtin_amdgcn_perm(rw[3], rw[2], kHighHalves)});
+  // Tokens past every taken row's end hold stale data: zero their V (0 * NaN); word 0 holds
+  // tokens 4h, 4h + 1 (low, high half), word 1 tokens 4h + 2, 4h + 3.
+  if (t_base + kBlockTokens > n_max) {
+    const int t0 = t_base + 4 * h;
+    const uint32_t m0 = (t0 < n_max ? 0x0000ffffu : 0u) | (t0 + 1 < n_max ? 0xffff0000u : 0u);
+    const uint32_t m1 = (t0 + 2 < n_max ? 0x0000ffffu : 0u) | (t0 + 3 < n_max ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int j = 0; j < Mg::kTiles; ++j) {
+      cur.vt[j][0] &= m0;
+      cur.vt[j][1] &= m1;
+    }
+  }
+  // P V: the 32-long k of the 16x16x32 product runs over (term, token), lane (c, h) giving
+  // P_hi[c][4h .. 4h + 3] then P_lo[c][4h .. 4h + 3]; the B operand is V[4h .. 4h + 3] twice.
+#pragma unroll
+  for (int j = 0; j < Mg::kTiles; ++j) {
+    const bf16x8_t b = __builtin_bit_cast(
+        bf16x8_t, u32x4_t{cur.vt[j][0], cur.vt[j][1], cur.vt[j][0], cur.vt[j][1]});
+    r.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, r.o[j], 0, 0, 0);
   }
 }
 
@@ -209,12 +298,12 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
   auto compute = [&](const LdsStage<D>& st, int b) {
     const int t_base = b * kBlockTokens;
     if (t_base >= n_wave) return;  // past every row of this wave (causal): nothing to add
-    MfmaBlock<D> cur;
-    stage_read<D>(cur, st, c, h);
+    TrBlock<D> cur;
+    stage_read_tr<D>(cur, st, c, h);
 #pragma unroll
     for (int r = 0; r < kR; ++r)
       if (t_base < tile_end[r])
-        mfma_rows_block<D>(rows[r], cur, qr[r], t_base, n_c[r], n_wave, h, scale_log2);
+        tr_rows_block<D>(rows[r], cur, qr[r], t_base, n_c[r], n_wave, h, scale_log2);
   };
 
   // Three LDS stages, three register sets: the loads of block j are issued two blocks
@@ -258,7 +347,7 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
   }
 
   // Row c's totals live on the four lanes with lane % 16 == c; output row 4h + i's on
-  // lane (c, h).  Each output row takes its max and sum from a lane owning its score row.
+  // lane (c, h), dims 16j + c.  Each output row takes its max and sum from a lane owning its score row.
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     float l_c = rows[r].l_part;
@@ -273,12 +362,10 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       const size_t sh =
           static_cast<size_t>(ch.r0 + t0 + rr / G) * num_q_heads + kvh * G + rr % G;
-      float* dst = out + sh * D + c * Mg::kTiles;
+      // output tile j holds dims 16j + c: each store writes 16 consecutive floats of a row
+      float* dst = out + sh * D + c;
 #pragma unroll
-      for (int u = 0; u < Mg::kTiles / 4; ++u)
-        *reinterpret_cast<float4*>(dst + 4 * u) =
-            make_float4(rows[r].o[4 * u][i] * inv, rows[r].o[4 * u + 1][i] * inv,
-                        rows[r].o[4 * u + 2][i] * inv, rows[r].o[4 * u + 3][i] * inv);
+      for (int j = 0; j < Mg::kTiles; ++j) dst[16 * j] = rows[r].o[j][i] * inv;
       if (c == 0 && lse != nullptr) lse[sh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
   }
