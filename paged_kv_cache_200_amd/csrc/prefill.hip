@@ -183,7 +183,11 @@ __device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    p[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - r.m_c);
+    // No select for masked scores: exp2(-inf - m) is 0 once m is finite, and every live
+    // row's m is finite from block 0 on (block 0 comes first and holds token 0, which every
+    // causal row attends).  Rows past the chunk's last token keep m = -inf and turn NaN;
+    // matrix-core rows are independent and those rows are never written.
+    p[i] = fast_exp2(x[i] - r.m_c);
     r.l_part += p[i];
   }
   uint32_t pw[4], rw[4];
