@@ -454,12 +454,13 @@ def main():
 
     def step():
         if in_pass:
-            # lengths advance once per step, so one plan serves every layer
-            pkv.decode_plan(ctx, tables, hq, d, max_ctx, P, workspace=step_plan)
+            # lengths advance once per step, so one plan serves every layer: the step-wide
+            # tensors are checked and planned once, then each layer is one checked launch
+            ds = pkv.DecodeStep(qs[0], kcs[0], vcs[0], k_new, v_new, tables, start, cu, ctx,
+                                max_ctx, scale=scale, partition_size=P, out=out, lse=lse,
+                                workspace=step_plan)
             for l in range(layers):
-                pkv.append_paged_decode_planned(qs[l], kcs[l], vcs[l], k_new, v_new, tables,
-                                                start, cu, ctx, max_ctx, step_plan, scale=scale,
-                                                partition_size=P, out=out, lse=lse)
+                ds.layer(qs[l], kcs[l], vcs[l], k_new, v_new)
             return
         for l in range(layers):
             if shared_path:

@@ -9,6 +9,7 @@ using the ops without it raises.
 
 from .ops import (  # noqa: F401
     BLOCK_SIZE,
+    DecodeStep,
     IN_PASS_MERGE_MAX_PARTITIONS,
     append_paged_decode,
     append_paged_decode_planned,

@@ -270,6 +270,89 @@ def append_paged_decode_planned(q, k_cache, v_cache, k_new, v_new, block_tables,
     return out, lse
 
 
+class DecodeStep:
+    """One decode step over the layers of a model: append_paged_decode_planned per layer,
+    with the host work of a call cut to what differs between layers.
+
+    The constructor takes the first layer's tensors and checks everything as
+    append_paged_decode_planned does.  The step-wide tensors (block tables, positions,
+    cu_new_tokens, context lengths, plan workspace, default outputs) are bound here, and
+    the work plan is written for them (plan=True).  layer() then checks only what a layer
+    brings: its q, caches and new K/V must have the first layer's shapes, dtype kind and
+    device, and be contiguous.  Each layer() is one pkv_append_paged_decode_planned launch,
+    with the same results as the function.
+
+    Bound tensors must stay allocated and keep their shapes while the object is used.
+    Their contents may change in place between steps; plan() must then run again before
+    the next layer().  Results go to the bound out/lse unless a layer passes its own.
+    """
+
+    def __init__(self, q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
+                 cu_new_tokens, context_lens, max_context_len, scale=None, partition_size=0,
+                 out=None, lse=None, want_lse=True, workspace=None, stream=None, plan=True):
+        B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+        _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        self.out, self.lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+        need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
+        self.workspace, wbytes = _workspace(workspace, need, q.device)
+        self.block_tables, self.start_pos = block_tables, start_pos
+        self.cu_new_tokens, self.context_lens = cu_new_tokens, context_lens
+        self.max_context_len = int(max_context_len)
+        self.partition_size = int(partition_size)
+        self.num_q_heads, self.head_dim = hq, d
+        self.stream = stream
+        self._q_shape, self._cache_shape, self._new_shape = q.shape, k_cache.shape, k_new.shape
+        self._out_shape, self._lse_shape = (B, hq, d), (B, hq)
+        self._kinds = (torch.float32,) if k_cache.dtype == torch.float32 else _BF16_TYPES
+        self._device = q.get_device()
+        self._fn = getattr(_lib.lib(), "pkv_append_paged_decode_planned")
+        self._fixed = (block_tables.data_ptr(), block_tables.shape[1], start_pos.data_ptr(),
+                       cu_new_tokens.data_ptr(), k_new.shape[0], context_lens.data_ptr(), B,
+                       hq, hkv, d, BLOCK_SIZE, nb, self.max_context_len, float(scale),
+                       self.partition_size, self.workspace.data_ptr(), wbytes,
+                       _kv_code(k_cache))
+        if plan:
+            self.plan()
+
+    def plan(self):
+        """(Re)write the work plan for the bound context lengths and tables."""
+        decode_plan(self.context_lens, self.block_tables, self.num_q_heads, self.head_dim,
+                    self.max_context_len, self.partition_size, workspace=self.workspace,
+                    stream=self.stream)
+
+    def _check(self, t, shape, kinds, what):
+        if (not isinstance(t, torch.Tensor) or t.shape != shape or t.dtype not in kinds
+                or t.get_device() != self._device or not t.is_contiguous()):
+            raise ValueError(f"{what} must be a contiguous tensor of shape {tuple(shape)} "
+                             f"and dtype {kinds[0]} on GPU {self._device}, like the first "
+                             f"layer's")
+
+    def layer(self, q, k_cache, v_cache, k_new, v_new, out=None, lse=None):
+        """Append this layer's new tokens to its caches and attend; returns (out, lse)."""
+        kinds = self._kinds
+        self._check(q, self._q_shape, kinds, "q")
+        self._check(k_cache, self._cache_shape, kinds, "k_cache")
+        self._check(v_cache, self._cache_shape, kinds, "v_cache")
+        self._check(k_new, self._new_shape, kinds, "k_new")
+        self._check(v_new, self._new_shape, kinds, "v_new")
+        if out is None:
+            out = self.out
+        else:
+            self._check(out, self._out_shape, (torch.float32,), "out")
+        if lse is None:
+            lse = self.lse
+        else:
+            self._check(lse, self._lse_shape, (torch.float32,), "lse")
+        s = torch.cuda.current_stream() if self.stream is None else self.stream
+        _lib.check("pkv_append_paged_decode_planned",
+                   self._fn(out.data_ptr(), None if lse is None else lse.data_ptr(),
+                            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            k_new.data_ptr(), v_new.data_ptr(), *self._fixed, s.cuda_stream))
+        return out, lse
+
+
 def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_starts,
                                group_shared_blocks, max_shared_blocks, max_context_len,
                                scale=None, partition_size=0, out=None, lse=None, workspace=None,

@@ -61,3 +61,20 @@ def test_host_only_calls():
     st = lib.pkv_kv_append(None, None, None, None, None, 1, None, None, 1, 0, 1, 64, 16, 4, 0,
                            None)
     assert st == 0  # nothing to append
+
+
+def test_decode_step_refuses_host_tensors():
+    """DecodeStep checks its first layer's tensors before it calls the library."""
+    import pytest
+    import torch
+    ensure_built()
+    import paged_kv_cache_200_amd as pkv
+    B, hq, hkv, d = 2, 4, 2, 64
+    q = torch.zeros(B, hq, d)
+    kc = torch.zeros(8, hkv, 16, d)
+    kn = torch.zeros(B, hkv, d)
+    i32 = dict(dtype=torch.int32)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        pkv.DecodeStep(q, kc, kc.clone(), kn, kn.clone(), torch.zeros(B, 4, **i32),
+                       torch.zeros(B, **i32), torch.arange(B + 1, **i32), torch.ones(B, **i32),
+                       1, partition_size=16)

@@ -631,3 +631,62 @@ def test_append_in_pass_over_layers_with_one_plan():
     assert flags & 2, flags
     after = dc.k.cpu().numpy()
     assert after.tobytes() != before  # the other sequences' tokens were written
+
+
+def test_decode_step_equals_planned_calls():
+    """DecodeStep (step-wide tensors bound and planned once, one layer() per layer) leaves
+    every layer's pool, out and lse equal to append_paged_decode_planned's, bit for bit;
+    after context lengths and positions change in place, plan() re-plans for them."""
+    say("decode step: qwen_gqa seed 2, 3 layers, 2 steps")
+    case = config_case("qwen_gqa", 2, layers=3, max_batch=24)
+    ops = _ops()
+    B, P = case.batch, 256
+    start = dev((case.context_lens - 1).astype(np.int32))
+    cu = dev(np.arange(B + 1, dtype=np.int32))
+    rng = np.random.default_rng(5)
+    a = [DeviceCase(case, layer) for layer in range(3)]
+    b = [DeviceCase(case, layer) for layer in range(3)]
+    ctx_a, ctx_b = a[0].ctx.clone(), b[0].ctx.clone()
+    tables = a[0].tables
+    news = []
+    for _ in range(6):
+        shape = (B, case.num_kv_heads, case.head_dim)
+        news.append((dev(bf16_bits(rng.standard_normal(shape).astype(np.float32))),
+                     dev(bf16_bits(rng.standard_normal(shape).astype(np.float32)))))
+    outs = [torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32,
+                        device="cuda") for _ in range(3)]
+    step = ops.DecodeStep(a[0].q, a[0].k, a[0].v, *news[0], tables, start, cu, ctx_a,
+                          a[0].max_ctx, scale=float(case.scale), partition_size=P)
+    for it in range(2):
+        if it == 1:
+            # the next step: shorter contexts, each new token at its sequence's last slot
+            shorter = torch.clamp(ctx_a - 3, min=1)
+            ctx_a.copy_(shorter)
+            ctx_b.copy_(shorter)
+            start.copy_(shorter - 1)
+            step.plan()
+        plan = ops.decode_plan(ctx_b, tables, case.num_q_heads, case.head_dim, b[0].max_ctx, P)
+        for layer in range(3):
+            kn, vn = news[3 * it + layer]
+            # layer 1 writes into its own output buffer, the others into the bound one
+            o1, l1 = step.layer(a[layer].q, a[layer].k, a[layer].v, kn, vn,
+                                out=outs[layer] if layer == 1 else None)
+            o1, l1 = o1.clone(), l1.clone()
+            o2, l2 = ops.append_paged_decode_planned(b[layer].q, b[layer].k, b[layer].v, kn, vn,
+                                                     tables, start, cu, ctx_b, b[0].max_ctx,
+                                                     plan, scale=float(case.scale),
+                                                     partition_size=P)
+            torch.cuda.synchronize()
+            tag = (it, layer)
+            assert a[layer].k.cpu().numpy().tobytes() == b[layer].k.cpu().numpy().tobytes(), tag
+            assert a[layer].v.cpu().numpy().tobytes() == b[layer].v.cpu().numpy().tobytes(), tag
+            assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes(), tag
+            assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes(), tag
+    assert_no_device_error()
+    # a layer whose tensors do not match the first layer's is refused on the host
+    with pytest.raises(ValueError):
+        step.layer(a[0].q[:-1], a[0].k, a[0].v, *news[0])
+    with pytest.raises(ValueError):
+        step.layer(a[0].q, a[0].k.float(), a[0].v, *news[0])
+    with pytest.raises(ValueError):
+        step.layer(a[0].q, a[0].k, a[0].v, news[0][0].cpu(), news[0][1])
