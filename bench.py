@@ -335,11 +335,13 @@ def run_replay(args, np, torch, pkv):
         d_ctx = dev_all[n * W + n:n * W + 2 * n]
         d_cu = dev_all[n * W + 2 * n:]
         max_ctx = int(pos.max()) + 1
+        # one work plan for the step, then one append + decode launch per layer
+        step = pkv.DecodeStep(q_all[t][0], kc[0], vc[0], *kv_all[t][0], d_tables, d_start,
+                              d_cu, d_ctx, max_ctx, partition_size=0, out=out[:n],
+                              want_lse=False, workspace=ws)
         for l in range(L):
             k, v = kv_all[t][l]
-            pkv.append_paged_decode(q_all[t][l], kc[l], vc[l], k, v, d_tables, d_start, d_cu,
-                                    d_ctx, max_ctx, partition_size=0, out=out[:n],
-                                    want_lse=False, workspace=ws)
+            step.layer(q_all[t][l], kc[l], vc[l], k, v)
             calls += 1
         ctxs = (pos + 1).astype(np.int64)
         total_tokens += L * int(ctxs.sum())
@@ -366,7 +368,8 @@ def run_replay(args, np, torch, pkv):
         "config": {"workload": "gpt2_replay", "seed": args.seed, "batch": B, "layers": L,
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
                    "num_blocks": nb, "steps": steps,
-                   "step": "host block manager + table upload + per layer append+decode"},
+                   "step": "host block manager + table upload + work plan, then per layer one "
+                           "append + decode launch"},
         "pct_of_hbm_peak": round(100 * total_bytes / wall / 1e9 / HBM_PEAK_GBPS, 3),
         "seq_tokens_per_s": round(total_tokens / wall, 1),
         "gpu_event_seconds": round(gpu_s, 5),

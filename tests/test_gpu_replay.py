@@ -32,8 +32,9 @@ def _nan_pool(shape):
 @pytest.mark.parametrize("seed", [0])
 def test_gpt2_replay(seed):
     """24 sequences admitted together; prompt appended as one multi-token write per
-    layer; then per step and layer a one-token append and a decode; a sequence's
-    blocks return to the pool after its last token.  Lengths advance once per step."""
+    layer; then per step and layer a one-token append and a decode (separate calls, or
+    one DecodeStep launch); a sequence's blocks return to the pool after its last token.
+    Lengths advance once per step."""
     from paged_kv_cache_200_amd import BlockManager
     import paged_kv_cache_200_amd as pkv
     sched = replay_schedule(seed)
@@ -75,12 +76,23 @@ def test_gpt2_replay(seed):
         cu1 = np.arange(len(active) + 1, dtype=np.int32)
         d_tables, d_ctx, d_start, d_cu = dev(tables), dev(ctx), dev(pos), dev(cu1)
         max_ctx = int(ctx.max())
+        # every third step as a serving loop runs it: one plan, then one append + decode
+        # launch per layer (DecodeStep); the other steps append and decode separately
+        step = None
         for layer in range(L):
             kn, vn = replay_step_values(sched, t, layer, active, "kv")
             q = replay_step_values(sched, t, layer, active, "q")
-            pkv.kv_append(kc[layer], vc[layer], dev(kn), dev(vn), d_tables, d_start, d_cu)
-            out, lse = pkv.paged_decode(dev(q), kc[layer], vc[layer], d_tables, d_ctx, max_ctx,
-                                        partition_size=64 if t % 2 else 0)
+            P = 64 if t % 2 else 0
+            if t % 3 == 2:
+                dq, dkn, dvn = dev(q), dev(kn), dev(vn)
+                if step is None:
+                    step = pkv.DecodeStep(dq, kc[layer], vc[layer], dkn, dvn, d_tables, d_start,
+                                          d_cu, d_ctx, max_ctx, partition_size=P)
+                out, lse = step.layer(dq, kc[layer], vc[layer], dkn, dvn)
+            else:
+                pkv.kv_append(kc[layer], vc[layer], dev(kn), dev(vn), d_tables, d_start, d_cu)
+                out, lse = pkv.paged_decode(dev(q), kc[layer], vc[layer], d_tables, d_ctx,
+                                            max_ctx, partition_size=P)
             pa.kv_append(host_k[layer], host_v[layer], kn, vn, tables, pos, cu1, inplace=True)
             want = pa.paged_decode(q, host_k[layer], host_v[layer], tables, ctx,
                                    np.float32(1 / 8.0), "f32")
