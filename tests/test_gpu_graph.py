@@ -1,6 +1,7 @@
 """Library calls captured in a HIP graph (torch.cuda.CUDAGraph) replay to the eager
 results, bit for bit, on every replay, with eager work and synchronisations between
-replays: multi-layer append + decode, the shared-prefix decode and the prefill."""
+replays: multi-layer append + decode (per-layer calls and DecodeStep), the shared-prefix decode
+and the prefill."""
 
 from __future__ import annotations
 
@@ -114,3 +115,32 @@ def test_graph_prefill():
                           lse=lse)
 
     _check_graph(step, [out, lse])
+
+
+def test_graph_decode_step():
+    """One plan per step and one launch per layer (DecodeStep), captured whole."""
+    import paged_kv_cache_200_amd as pkv
+    say("graph: DecodeStep, plan + 4 layers, Qwen shape")
+    case = config_case("qwen_gqa", 1, layers=4)
+    B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    qs = [dev(case.q[l]) for l in range(4)]
+    ks = [dev(case.k_pool[l]) for l in range(4)]
+    vs = [dev(case.v_pool[l]) for l in range(4)]
+    tables, ctx = dev(case.block_tables), dev(case.context_lens)
+    mx = int(case.context_lens.max())
+    rng = np.random.default_rng(4)
+    kn = dev(bf16_bits(rng.standard_normal((B, hkv, d)).astype(np.float32)))
+    vn = dev(bf16_bits(rng.standard_normal((B, hkv, d)).astype(np.float32)))
+    start = dev((case.context_lens - 1).astype(np.int32))
+    cu = dev(np.arange(B + 1, dtype=np.int32))
+    outs = [torch.empty((B, hq, d), dtype=torch.float32, device="cuda") for _ in range(4)]
+    lses = [torch.empty((B, hq), dtype=torch.float32, device="cuda") for _ in range(4)]
+    ds = pkv.DecodeStep(qs[0], ks[0], vs[0], kn, vn, tables, start, cu, ctx, mx,
+                        scale=float(case.scale), partition_size=256, plan=False)
+
+    def step():
+        ds.plan()
+        for l in range(4):
+            ds.layer(qs[l], ks[l], vs[l], kn, vn, out=outs[l], lse=lses[l])
+
+    _check_graph(step, outs + lses)
