@@ -325,9 +325,9 @@ class DecodeStep:
     def _check(self, t, shape, kinds, what):
         if (not isinstance(t, torch.Tensor) or t.shape != shape or t.dtype not in kinds
                 or t.get_device() != self._device or not t.is_contiguous()):
-            raise ValueError(f"{what} must be a contiguous tensor of shape {tuple(shape)} "
-                             f"and dtype {kinds[0]} on GPU {self._device}, like the first "
-                             f"layer's")
+            kind = "float32" if kinds[0] == torch.float32 else "bfloat16 (or its bits)"
+            raise ValueError(f"{what} must be a contiguous {kind} tensor of shape "
+                             f"{tuple(shape)} on GPU {self._device}, like the first layer's")
 
     def layer(self, q, k_cache, v_cache, k_new, v_new, out=None, lse=None):
         """Append this layer's new tokens to its caches and attend; returns (out, lse)."""
