@@ -633,14 +633,20 @@ def test_append_in_pass_over_layers_with_one_plan():
     assert after.tobytes() != before  # the other sequences' tokens were written
 
 
-def test_decode_step_equals_planned_calls():
+@pytest.mark.parametrize("shape", ["qwen_bf16_P256", "f32_d128_P0"])
+def test_decode_step_equals_planned_calls(shape):
     """DecodeStep (step-wide tensors bound and planned once, one layer() per layer) leaves
     every layer's pool, out and lse equal to append_paged_decode_planned's, bit for bit;
     after context lengths and positions change in place, plan() re-plans for them."""
-    say("decode step: qwen_gqa seed 2, 3 layers, 2 steps")
-    case = config_case("qwen_gqa", 2, layers=3, max_batch=24)
+    say(f"decode step: {shape}, 3 layers, 2 steps")
+    if shape == "qwen_bf16_P256":
+        case, P = config_case("qwen_gqa", 2, layers=3, max_batch=24), 256
+    else:
+        case = build_case("step", [1, 16, 17, 300, 1000, 33, 64, 2], 16, 4, 128, "f32", seed=8,
+                          layers=3)
+        P = 0
     ops = _ops()
-    B, P = case.batch, 256
+    B = case.batch
     start = dev((case.context_lens - 1).astype(np.int32))
     cu = dev(np.arange(B + 1, dtype=np.int32))
     rng = np.random.default_rng(5)
@@ -649,10 +655,11 @@ def test_decode_step_equals_planned_calls():
     ctx_a, ctx_b = a[0].ctx.clone(), b[0].ctx.clone()
     tables = a[0].tables
     news = []
+    conv = bf16_bits if case.kv_dtype == "bf16" else (lambda x: x)
     for _ in range(6):
-        shape = (B, case.num_kv_heads, case.head_dim)
-        news.append((dev(bf16_bits(rng.standard_normal(shape).astype(np.float32))),
-                     dev(bf16_bits(rng.standard_normal(shape).astype(np.float32)))))
+        dims = (B, case.num_kv_heads, case.head_dim)
+        news.append((dev(conv(rng.standard_normal(dims).astype(np.float32))),
+                     dev(conv(rng.standard_normal(dims).astype(np.float32)))))
     outs = [torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32,
                         device="cuda") for _ in range(3)]
     step = ops.DecodeStep(a[0].q, a[0].k, a[0].v, *news[0], tables, start, cu, ctx_a,
@@ -687,6 +694,6 @@ def test_decode_step_equals_planned_calls():
     with pytest.raises(ValueError):
         step.layer(a[0].q[:-1], a[0].k, a[0].v, *news[0])
     with pytest.raises(ValueError):
-        step.layer(a[0].q, a[0].k.float(), a[0].v, *news[0])
+        step.layer(a[0].q, a[0].k.half(), a[0].v, *news[0])
     with pytest.raises(ValueError):
         step.layer(a[0].q, a[0].k, a[0].v, news[0][0].cpu(), news[0][1])
