@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 # HBM traffic records (rocprofv3 counters) of the first pass, per workload
 TRAFFIC_FILES = {w: os.path.join(ROOT, "profiles", f"traffic_{w}.json")
-                 for w in ("high_concurrency", "long_context")}
+                 for w in ("high_concurrency", "long_context", "qwen_gqa")}
 # the sources that define the first pass (and the plan/append prologue of its step);
 # counters taken on other sources are not reported
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
