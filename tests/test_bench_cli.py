@@ -29,3 +29,25 @@ def test_defaults():
                                                                        None, False, False)
     assert a.append_in_pass == "auto"
     assert a.steps * 0.25e-3 < 60   # the default timed region stays well under a minute
+
+
+def test_traffic_records_are_consistent():
+    """Each committed counter record's bytes follow from its own readings and scales, and
+    its scales from its calibration copies (512 MiB moved each way per copy)."""
+    import json
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    assert set(bench.TRAFFIC_FILES) >= {"high_concurrency", "long_context", "qwen_gqa"}
+    for workload, path in bench.TRAFFIC_FILES.items():
+        info = json.load(open(path))
+        kib = (info["fetch_size_kib_per_launch"] * info["fetch_scale"]
+               + info["write_size_kib_per_launch"] * info["write_scale"])
+        assert abs(kib * 1024 - info["bytes_per_launch"]) < 2048, workload
+        ratio = info["bytes_per_launch"] / info["algorithmic_bytes_per_launch"]
+        assert abs(ratio - info["traffic_over_algorithmic"]) < 1e-4, workload
+        fetch = re.search(r"FETCH_SIZE ([\d. /]+) KiB", info["calibration"]).group(1)
+        readings = [float(x) for x in fetch.split("/")]
+        assert abs(524288.0 * len(readings) / sum(readings) - info["fetch_scale"]) < 1e-4, workload
+        assert info["partition_size"] > 0 and info["seed"] == 0
+        assert len(info["kernel_source_sha256"]) == 64
