@@ -279,8 +279,9 @@ class DecodeStep:
     cu_new_tokens, context lengths, plan workspace, default outputs) are bound here, and
     the work plan is written for them (plan=True).  layer() then checks only what a layer
     brings: its q, caches and new K/V must have the first layer's shapes, dtype kind and
-    device, and be contiguous.  Each layer() is one pkv_append_paged_decode_planned launch,
-    with the same results as the function.
+    device, and be contiguous.  Each layer() is one pkv_append_paged_decode_planned call
+    (a single launch while no sequence has more than IN_PASS_MERGE_MAX_PARTITIONS
+    partitions), with the same results as the function.
 
     Bound tensors must stay allocated and keep their shapes while the object is used.
     Their contents may change in place between steps; plan() must then run again before
