@@ -1,7 +1,7 @@
 """The exact library calls bench.py times, at the workloads' full sizes, against the oracle:
 the 256-sequence decode step (append + decode in one call, partition 4096), the
 copy-on-write fork step (append + shared-prefix decode, partition 1024) and the chunked
-prefill (sampled sequences)."""
+prefill (every sequence, sampled query rows)."""
 
 from __future__ import annotations
 
@@ -31,19 +31,27 @@ def _oracle_step(case, si):
                            case.kv_dtype)
 
 
-def test_high_concurrency_step_as_benched():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_high_concurrency_step_as_benched(seed):
+    """Seeds 0-2: seed 1 holds an 8192-token sequence, exactly two full partitions."""
     import paged_kv_cache_200_amd as pkv
-    say("bench config: high_concurrency, append_paged_decode, P=4096")
-    case = config_case("high_concurrency", 0)
-    si = decode_step_inputs(case, 0)
+    say(f"bench config: high_concurrency seed {seed}, append_paged_decode, P=4096")
+    case = config_case("high_concurrency", seed)
+    si = decode_step_inputs(case, seed)
     k, v = dev(case.k_pool[0]), dev(case.v_pool[0])
     o, l = pkv.append_paged_decode(dev(case.q[0]), k, v, dev(si.k_new), dev(si.v_new),
                                    dev(case.block_tables), dev(si.start_pos), dev(si.cu_new),
                                    dev(case.context_lens), int(case.context_lens.max()),
                                    scale=float(case.scale), partition_size=4096)
     torch.cuda.synchronize()
-    assert_parity((o.cpu().numpy(), l.cpu().numpy()), _oracle_step(case, si), "bf16",
-                  "high_concurrency as benched")
+    kp, vp = pa.kv_append(case.k_pool[0], case.v_pool[0], si.k_new, si.v_new,
+                          case.block_tables, si.start_pos, si.cu_new)
+    assert k.cpu().numpy().tobytes() == kp.tobytes(), "K pool after the append"
+    assert v.cpu().numpy().tobytes() == vp.tobytes(), "V pool after the append"
+    assert_parity((o.cpu().numpy(), l.cpu().numpy()),
+                  pa.paged_decode(case.q[0], kp, vp, case.block_tables, case.context_lens,
+                                  case.scale, case.kv_dtype),
+                  "bf16", f"high_concurrency s{seed} as benched")
     assert_no_device_error()
 
 
@@ -65,9 +73,9 @@ def test_prefix_fork_step_as_benched():
     assert_no_device_error()
 
 
-def test_chunked_prefill_as_benched_sampled():
+def test_chunked_prefill_as_benched():
     import paged_kv_cache_200_amd as pkv
-    say("bench config: chunked_prefill, kv_append + paged_prefill, sampled sequences")
+    say("bench config: chunked_prefill, kv_append + paged_prefill, every sequence")
     pc = chunked_prefill_case(0)
     case = pc.case
     k, v = dev(case.k_pool[0]), dev(case.v_pool[0])
@@ -79,12 +87,21 @@ def test_chunked_prefill_as_benched_sampled():
     o, l = o.cpu().numpy(), l.cpu().numpy()
     kp, vp = pa.kv_append(case.k_pool[0], case.v_pool[0], pc.k_new, pc.v_new,
                           case.block_tables, pc.start_pos, pc.cu_q)
-    # the longest and the shortest context, whole chunks each
-    order = np.argsort(case.context_lens)
-    for s in (int(order[-1]), int(order[0])):
+    # every sequence; of each chunk the first and last four query rows and 24 drawn ones.
+    # Query i of a chunk of L at context n attends tokens [0, n - L + i]: the oracle takes
+    # it as a one-token chunk of the context cut to n - L + i + 1 tokens.
+    rng = np.random.default_rng(0)
+    for s in range(case.batch):
         r0, r1 = int(pc.cu_q[s]), int(pc.cu_q[s + 1])
-        want = pp.paged_prefill(pc.q[r0:r1], kp, vp, case.block_tables[s:s + 1],
-                                np.array([0, r1 - r0], np.int32), case.context_lens[s:s + 1],
-                                case.scale, "bf16")
-        assert_parity((o[r0:r1], l[r0:r1]), want, "bf16", f"chunked prefill seq {s}")
+        L, n = r1 - r0, int(case.context_lens[s])
+        rows = sorted(set(range(4)) | set(range(L - 4, L)) | set(rng.integers(0, L, 24).tolist()))
+        got_o, got_l, want_o, want_l = [], [], [], []
+        for i in rows:
+            wo, wl = pp.paged_prefill(pc.q[r0 + i:r0 + i + 1], kp, vp, case.block_tables[s:s + 1],
+                                      np.array([0, 1], np.int32),
+                                      np.array([n - L + i + 1], np.int32), case.scale, "bf16")
+            got_o.append(o[r0 + i]); got_l.append(l[r0 + i])
+            want_o.append(wo[0]); want_l.append(wl[0])
+        assert_parity((np.array(got_o), np.array(got_l)), (np.array(want_o), np.array(want_l)),
+                      "bf16", f"chunked prefill seq {s} ({len(rows)} rows)")
     assert_no_device_error()
