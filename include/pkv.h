@@ -7,9 +7,9 @@
  *     (16 tokens) drawn from a shared pool and are addressed through a
  *     per-sequence block table; forked sequences share blocks copy-on-write
  *     through reference counts.
- *   - spindle, "Two bugs worth recording": append takes an explicit start
- *     position, gather takes an explicit length, and the caller (not the
- *     cache) advances lengths, once per step.  Nothing here ever infers or
+ *   - spindle, "Two bugs worth recording": where a write lands and how many
+ *     tokens a read covers are arguments, and lengths move forward in the
+ *     caller, once per step, never in the cache.  Nothing here ever infers or
  *     advances a length.
  *   - mlsystems topic listing, flash-decoding entry: at q_len = 1 the KV
  *     length is split into partitions processed in parallel, whose partial
@@ -92,8 +92,8 @@ int pkv_version(void);
 const char* pkv_status_string(int status);
 
 /*
- * KV append (spindle, "Two bugs worth recording": append takes an explicit
- * start position).
+ * KV append (spindle, "Two bugs worth recording": the write position is an
+ * argument, never derived from a stored length).
  *
  * For each sequence s and i in [0, cu_new_tokens[s+1] - cu_new_tokens[s]):
  *   pos = start_pos[s] + i,
@@ -167,7 +167,14 @@ int pkv_decode_plan(void* workspace, size_t workspace_bytes, const int32_t* cont
  * bit.  Past 8 partitions per sequence the merge is a second launch (the
  * combine kernel, same result), whose rows run in parallel.  Sequences that
  * fit in one partition are written directly.  Calls
- * that overlap in time must not share a workspace.  The result does not depend on
+ * that overlap in time must not share a workspace.  Ordering of the in-launch
+ * merge: each split unit writes its partial result with device-scope stores,
+ * waits until they have completed, then takes a ticket from a device-scope
+ * counter with a relaxed atomic; the last ticket's workgroup reads the slots with
+ * device-scope loads.  There is no release/acquire fence (on gfx950 those write
+ * back and invalidate the whole L2 of an XCD); the ordering rests on how gfx950
+ * completes device-scope stores before the wait returns, which is why the
+ * library builds for gfx950 only.  The result does not depend on
  * the batch: a sequence decoded alone or in any batch, with the same
  * partition_size, gives bit-identical out and lse.
  * lse may be NULL.  workspace: pkv_decode_workspace_bytes(...) bytes,

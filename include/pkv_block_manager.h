@@ -1,10 +1,11 @@
 /*
  * pkv_block_manager.h - host-side bookkeeping of the paged KV pool.
  *
- * spindle, "Paging": a pool of fixed-size blocks and a per-sequence block
- * table; a sequence takes blocks on demand so waste is bounded by its final
- * partial block; reference counts give copy-on-write forking (four sequences
- * forked from a 16-token parent hold 64 logical tokens in 16 physical slots).
+ * spindle, "Paging": one pool of fixed-size blocks, a table per sequence
+ * listing its blocks, blocks taken only as tokens arrive (so a sequence wastes
+ * at most its last, partly filled block), and blocks shared by reference count
+ * between forks (copy-on-write); the page's example is a 16-token parent forked
+ * four ways: 64 tokens attended, 16 stored.
  * spindle, "Two bugs worth recording": the cache never infers a length; the
  * caller names the token range it is about to write.
  *

@@ -7,8 +7,9 @@ computes, written from the pages' statement of the problem:
   table; reference counts give copy-on-write forking.
 * spindle ("Why write the forward pass"): batched decoding must equal decoding
   each sequence alone (no attention leaking across sequences).
-* spindle ("Two bugs worth recording"): append takes an explicit start
-  position, gather takes an explicit length.
+* spindle ("Two bugs worth recording"): the cache never works out a length
+  itself; the position of a write and the number of tokens a read covers are
+  both passed in by the caller.
 * the mlsystems topic listing (flash-decoding entry): KV-length-parallel
   decode whose partial results are merged afterwards.
 

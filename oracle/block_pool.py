@@ -1,10 +1,10 @@
 """Plain-Python model of the block pool (test infrastructure only).
 
-spindle ("Paging") describes the allocator: a pool of fixed-size blocks, a
-per-sequence block table, waste bounded by the final partial block, and
-reference counts that give copy-on-write forking.  Its worked example: four
-sequences forked from a 16-token parent hold 64 logical tokens in 16 physical
-slots.
+spindle ("Paging") describes the allocator: fixed-size blocks handed out from one
+pool, each sequence finding its blocks through its own table, so at most the last,
+partly filled block of a sequence is wasted; forks share blocks by reference count
+(copy-on-write).  The page's worked example: a 16-token parent forked into four
+sequences gives them 64 tokens to attend while the pool stores only 16.
 
 Readings where the page is silent:
 * the free list is FIFO over a given initial order; freed blocks go to its tail;

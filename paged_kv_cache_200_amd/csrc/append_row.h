@@ -1,6 +1,6 @@
 // One wavefront writes one new token's K and V rows (every KV head) into the cache at
-// its explicit position (spindle, "Two bugs worth recording": append takes an explicit
-// start position).  Shared by the standalone append kernel and the decode prologue.
+// the position the caller names (spindle, "Two bugs worth recording": the write position
+// is an argument, never derived from a stored length).  Shared by the standalone append kernel and the decode prologue.
 // The including file defines the device error word used by PKV_FLAG_ERROR.
 #pragma once
 

@@ -31,6 +31,16 @@
 
 #include "common.h"
 
+// The merge of split sequences inside the first pass orders its partial-result stores
+// before the merge ticket without a release/acquire pair: device-scope (sc1) stores, a
+// wait for their completion and a relaxed device-scope ticket, read back through
+// device-scope loads.  That this suffices is a property of how gfx950 executes those
+// instructions, not a guarantee of the HIP memory model, so the file builds for gfx950
+// only.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "paged_decode.hip: the in-pass merge's memory ordering is established for gfx950 only"
+#endif
+
 PKV_DEFINE_ERROR_WORD(decode)
 
 #include "append_row.h"

@@ -1,8 +1,11 @@
 """Torch-tensor front end of libpkv: argument marshalling only.
 
 Every function checks the tensors' device, dtype, shape and contiguity, then
-passes raw device pointers and sizes to the C ABI, enqueued on torch's current
-HIP stream.  All computation happens in the library's kernels.
+passes raw device pointers and sizes to the C ABI, enqueued on the `stream`
+argument (default: torch's current HIP stream).  Outputs and workspaces the
+wrapper allocates itself are recorded on that stream, so the caching allocator
+does not reuse them while its kernels still run.  All computation happens in
+the library's kernels.
 
 bfloat16 data may be given as torch.bfloat16 or as torch.uint16/int16 bit
 patterns.
@@ -51,6 +54,15 @@ def _gpu(t: torch.Tensor, what: str, dtype=None, contiguous=True):
 def _stream(stream=None) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _held(t, stream):
+    """A tensor the wrapper allocated, used by kernels on `stream`: when that is not torch's
+    current stream, tell the caching allocator, so the memory is not handed out again
+    before the stream's work on it is done."""
+    if t is not None and stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
 
 
 def _ptr(t):
@@ -117,9 +129,9 @@ def _decode_checks(q, k_cache, v_cache, block_tables, context_lens):
     return B, hq, hkv, d, nb
 
 
-def _workspace(workspace, need, device):
+def _workspace(workspace, need, device, stream=None):
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        workspace = _held(torch.empty(max(need, 1), dtype=torch.uint8, device=device), stream)
     _gpu(workspace, "workspace")
     wbytes = workspace.numel() * workspace.element_size()
     if wbytes < need:
@@ -136,7 +148,7 @@ def decode_plan(context_lens, block_tables, num_q_heads, head_dim, max_context_l
     _gpu(block_tables, "block_tables", torch.int32)
     B = context_lens.shape[0]
     need = decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_size)
-    workspace, wbytes = _workspace(workspace, need, context_lens.device)
+    workspace, wbytes = _workspace(workspace, need, context_lens.device, stream)
     _lib.call("pkv_decode_plan", _ptr(workspace), wbytes, _ptr(context_lens),
               block_tables.shape[1], B, num_q_heads, head_dim, int(max_context_len),
               int(partition_size), _stream(stream))
@@ -148,15 +160,9 @@ def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_contex
     B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
-    _gpu(out, "out", torch.float32)
-    if lse is None and want_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _gpu(lse, "lse", torch.float32)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device, stream)
     need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
-    workspace, wbytes = _workspace(workspace, need, q.device)
+    workspace, wbytes = _workspace(workspace, need, q.device, stream)
     _lib.call(fn_name, _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
               _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d,
               BLOCK_SIZE, nb, int(max_context_len), float(scale), int(partition_size),
@@ -208,12 +214,12 @@ def _group_checks(group_starts, group_shared_blocks):
     return G
 
 
-def _outputs(out, lse, want_lse, B, hq, d, device):
+def _outputs(out, lse, want_lse, B, hq, d, device, stream=None):
     if out is None:
-        out = torch.empty((B, hq, d), dtype=torch.float32, device=device)
+        out = _held(torch.empty((B, hq, d), dtype=torch.float32, device=device), stream)
     _gpu(out, "out", torch.float32)
     if lse is None and want_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=device)
+        lse = _held(torch.empty((B, hq), dtype=torch.float32, device=device), stream)
     if lse is not None:
         _gpu(lse, "lse", torch.float32)
     return out, lse
@@ -231,9 +237,9 @@ def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_p
     _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device, stream)
     need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
-    workspace, wbytes = _workspace(workspace, need, q.device)
+    workspace, wbytes = _workspace(workspace, need, q.device, stream)
     _lib.call("pkv_append_paged_decode", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
               _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
               block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
@@ -258,9 +264,9 @@ def append_paged_decode_planned(q, k_cache, v_cache, k_new, v_new, block_tables,
     _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device, stream)
     need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
-    workspace, wbytes = _workspace(workspace, need, q.device)
+    workspace, wbytes = _workspace(workspace, need, q.device, stream)
     _lib.call("pkv_append_paged_decode_planned", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
               _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
               block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
@@ -295,9 +301,9 @@ class DecodeStep:
         _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
         if scale is None:
             scale = 1.0 / math.sqrt(d)
-        self.out, self.lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+        self.out, self.lse = _outputs(out, lse, want_lse, B, hq, d, q.device, stream)
         need = decode_workspace_bytes(B, hq, d, max_context_len, partition_size)
-        self.workspace, wbytes = _workspace(workspace, need, q.device)
+        self.workspace, wbytes = _workspace(workspace, need, q.device, stream)
         self.block_tables, self.start_pos = block_tables, start_pos
         self.cu_new_tokens, self.context_lens = cu_new_tokens, context_lens
         self.max_context_len = int(max_context_len)
@@ -364,9 +370,9 @@ def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, 
     G = _group_checks(group_starts, group_shared_blocks)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device, stream)
     need = shared_prefix_workspace_bytes(B, hq, d, int(max_context_len), int(partition_size))
-    workspace, wbytes = _workspace(workspace, need, q.device)
+    workspace, wbytes = _workspace(workspace, need, q.device, stream)
     _lib.call("pkv_paged_decode_shared_prefix", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
               _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
               _ptr(group_starts), _ptr(group_shared_blocks), G, int(max_shared_blocks), B, hq,
@@ -387,9 +393,9 @@ def append_paged_decode_shared_prefix(q, k_cache, v_cache, k_new, v_new, block_t
     G = _group_checks(group_starts, group_shared_blocks)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device)
+    out, lse = _outputs(out, lse, want_lse, B, hq, d, q.device, stream)
     need = shared_prefix_workspace_bytes(B, hq, d, int(max_context_len), int(partition_size))
-    workspace, wbytes = _workspace(workspace, need, q.device)
+    workspace, wbytes = _workspace(workspace, need, q.device, stream)
     _lib.call("pkv_append_paged_decode_shared_prefix", _ptr(out), _ptr(lse), _ptr(q),
               _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
               block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
@@ -424,10 +430,10 @@ def paged_prefill(q, k_cache, v_cache, block_tables, cu_q, context_lens, max_q_l
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+        out = _held(torch.empty((T, hq, d), dtype=torch.float32, device=q.device), stream)
     _gpu(out, "out", torch.float32)
     if lse is None and want_lse:
-        lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+        lse = _held(torch.empty((T, hq), dtype=torch.float32, device=q.device), stream)
     if lse is not None:
         _gpu(lse, "lse", torch.float32)
     _lib.call("pkv_paged_prefill", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -454,9 +460,11 @@ def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_c
     if max_partitions is None:
         max_partitions = np_
     if part_out is None:
-        part_out = torch.empty((B, hq, max_partitions, d), dtype=torch.float32, device=q.device)
+        part_out = _held(torch.empty((B, hq, max_partitions, d), dtype=torch.float32,
+                                     device=q.device), stream)
     if part_lse is None:
-        part_lse = torch.empty((B, hq, max_partitions), dtype=torch.float32, device=q.device)
+        part_lse = _held(torch.empty((B, hq, max_partitions), dtype=torch.float32,
+                                     device=q.device), stream)
     _gpu(part_out, "part_out", torch.float32)
     _gpu(part_lse, "part_lse", torch.float32)
     _lib.call("pkv_paged_decode_partials", _ptr(part_out), _ptr(part_lse), _ptr(q),
@@ -477,9 +485,9 @@ def lse_combine(part_out, part_lse, context_lens, partition_size, out=None, lse=
         raise ValueError("part_out [B, Hq, NP, D] and part_lse [B, Hq, NP] expected")
     B, hq, np_, d = part_out.shape
     if out is None:
-        out = torch.empty((B, hq, d), dtype=torch.float32, device=part_out.device)
+        out = _held(torch.empty((B, hq, d), dtype=torch.float32, device=part_out.device), stream)
     if lse is None and want_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=part_out.device)
+        lse = _held(torch.empty((B, hq), dtype=torch.float32, device=part_out.device), stream)
     _gpu(out, "out", torch.float32)
     _lib.call("pkv_lse_combine", _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
               _ptr(context_lens), B, hq, d, int(partition_size), np_, _stream(stream))

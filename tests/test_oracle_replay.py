@@ -24,8 +24,9 @@ def check_single_request(m):
 
 
 def check_stop_at_20_of_192(m):
-    """The page's example: a request that stops at 20 of a possible 192 tokens held all
-    192 (here prompt 4 + 192) for its whole lifetime; the pool held only what it used."""
+    """The page's example: a contiguous buffer reserved for 192 new tokens stays reserved
+    in full (here prompt 4 + 192) while its request produces only 20; the pool holds only
+    what the request has written."""
     c = m.replay(m.CONTIGUOUS, [4], [20], 192, 8192)
     assert c.slots_trace == [196] * 20
     assert c.tokens_trace == list(range(5, 25))
