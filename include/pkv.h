@@ -72,8 +72,13 @@ enum pkv_status {
   PKV_ERR_LAUNCH = -5,        /* the HIP runtime rejected a launch              */
   PKV_ERR_DEVICE = -6,        /* a HIP runtime call failed                      */
   PKV_ERR_OUT_OF_BLOCKS = -7, /* block manager: pool exhausted (nothing changed)*/
-  PKV_ERR_ARG = -8            /* bad argument value (alignment, range, id)      */
+  PKV_ERR_ARG = -8,           /* bad argument value (alignment, range, id)      */
+  PKV_ERR_SCRATCH = -9        /* needs more than PKV_STATIC_SCRATCH_BYTES       */
 };
+
+/* Size of the library's static per-device scratch buffer (see
+ * pkv_append_paged_decode_static). */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* Bits of the device error word. */
 enum pkv_device_error_bits {
@@ -208,6 +213,32 @@ int pkv_append_paged_decode(float* out, float* lse, const void* q, void* k_cache
                             int32_t num_blocks, int32_t max_context_len, float scale,
                             int32_t partition_size, void* workspace, size_t workspace_bytes,
                             int32_t dtype, pkv_stream_t stream);
+
+/*
+ * pkv_append_paged_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc.  Nothing is allocated: the plan,
+ * partial results and merge counters live in a static device array of
+ * PKV_STATIC_SCRATCH_BYTES bytes per GPU, which the library holds until the
+ * process ends.  Its device address is looked up once per device, on the first
+ * call made with that device current.  Arguments, results and device errors are
+ * those of pkv_append_paged_decode.  A call whose workspace
+ * (pkv_decode_workspace_bytes of the same sizes) would exceed
+ * PKV_STATIC_SCRATCH_BYTES returns PKV_ERR_SCRATCH and enqueues nothing.  Every
+ * call on one GPU uses the same array, and each call rewrites what it reads
+ * (its plan and merge counters are set by its own first launch): calls that
+ * overlap in time on one GPU (two streams, or two host threads) race and must
+ * be serialised by the caller.
+ */
+int pkv_append_paged_decode_static(float* out, float* lse, const void* q, void* k_cache,
+                                   void* v_cache, const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, int64_t bt_stride,
+                                   const int32_t* start_pos, const int32_t* cu_new_tokens,
+                                   int32_t total_new, const int32_t* context_lens,
+                                   int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_context_len, float scale,
+                                   int32_t partition_size, int32_t dtype, pkv_stream_t stream);
 
 /*
  * One decode step of one layer in one launch, on a plan made beforehand: exactly

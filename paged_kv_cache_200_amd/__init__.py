@@ -13,6 +13,8 @@ from .ops import (  # noqa: F401
     IN_PASS_MERGE_MAX_PARTITIONS,
     append_paged_decode,
     append_paged_decode_planned,
+    append_paged_decode_static,
+    STATIC_SCRATCH_BYTES,
     append_paged_decode_shared_prefix,
     copy_blocks,
     decode_plan,

@@ -22,6 +22,9 @@ PKV_BF16 = 1
 
 PKV_OK = 0
 PKV_ERR_OUT_OF_BLOCKS = -7
+PKV_ERR_SCRATCH = -9
+# size of the library's static per-device scratch array (PKV_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 16 << 20
 
 DEVICE_ERROR_BITS = {
     1: "block id out of range",
@@ -56,6 +59,10 @@ SIGNATURES = {
     "pkv_append_paged_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                                                _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_append_paged_decode_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                                      _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                                      _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                                      _vp]),
     "pkv_append_paged_decode_planned": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                        _i64, _vp, _vp, _i32, _vp, _i32, _i32,
                                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32,

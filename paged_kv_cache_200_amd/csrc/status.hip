@@ -15,6 +15,7 @@ extern "C" const char* pkv_status_string(int status) {
     case PKV_ERR_DEVICE: return "HIP runtime call failed";
     case PKV_ERR_OUT_OF_BLOCKS: return "block pool exhausted";
     case PKV_ERR_ARG: return "bad argument value";
+    case PKV_ERR_SCRATCH: return "the call needs more than the static scratch buffer holds";
     default: return "unknown status";
   }
 }

@@ -249,6 +249,32 @@ def append_paged_decode(q, k_cache, v_cache, k_new, v_new, block_tables, start_p
     return out, lse
 
 
+def append_paged_decode_static(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
+                               cu_new_tokens, context_lens, max_context_len, out, lse=None,
+                               scale=None, partition_size=0, stream=None):
+    """append_paged_decode with no workspace and no allocation: the library's static
+    per-GPU scratch array (STATIC_SCRATCH_BYTES) holds the plan and partial results, and
+    out (and lse, optional) must be given.  Calls that overlap in time on one GPU race."""
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+    _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
+    if out is None:
+        raise ValueError("append_paged_decode_static allocates nothing: pass out")
+    _gpu(out, "out", torch.float32)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _lib.call("pkv_append_paged_decode_static", _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
+              _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+              block_tables.shape[1], _ptr(start_pos), _ptr(cu_new_tokens), k_new.shape[0],
+              _ptr(context_lens), B, hq, hkv, d, BLOCK_SIZE, nb, int(max_context_len),
+              float(scale), int(partition_size), _kv_code(k_cache), _stream(stream))
+    return out, lse
+
+
+STATIC_SCRATCH_BYTES = _lib.STATIC_SCRATCH_BYTES
+
+
 def append_paged_decode_planned(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
                                 cu_new_tokens, context_lens, max_context_len, workspace,
                                 scale=None, partition_size=0, out=None, lse=None,
