@@ -72,6 +72,14 @@ def parse_args():
     p.add_argument("--graph", action="store_true",
                    help="replay the step as one captured HIP graph instead of launching "
                         "every library call from Python (measured no faster here)")
+    p.add_argument("--decode-path", choices=["valu", "mfma"], default="valu",
+                   help="plain (non-fork) workloads: valu = the first pass (default); mfma = "
+                        "the matrix-core tile of the shared-prefix path with every sequence a "
+                        "group of one (the dense-tile variant, for comparison)")
+    p.add_argument("--crossover", action="store_true",
+                   help="instead of one workload: sweep batch x context x partition size on "
+                        "uniform-length bf16 workloads (32/8 heads, head_dim 128) and print "
+                        "where splitting the KV length pays")
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="decode fork workloads with the plain path (each fork re-reads the "
                         "shared prefix) instead of the shared-prefix path")
@@ -380,6 +388,77 @@ def run_replay(args, np, torch, pkv):
     }
 
 
+CROSSOVER_BATCHES = (1, 4, 16, 64, 256)
+CROSSOVER_CONTEXTS = (512, 2048, 8192, 32768)
+CROSSOVER_PARTS = (0, 256, 512, 1024, 2048, 4096, 8192)
+CROSSOVER_MAX_TOKENS = 1 << 21  # 8.6 GB of bf16 K+V at 8 KV heads x 128 dims
+
+
+def run_crossover(args, np, torch, pkv):
+    """Decode-call time (plan + first pass + combine when needed) for uniform-length bf16
+    workloads (32 query / 8 KV heads, head_dim 128, blocks randomly permuted), over batch x
+    context x partition size (0 = one unit per sequence and KV head)."""
+    hq, hkv, d = 32, 8, 128
+    rows = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed)
+    for B in CROSSOVER_BATCHES:
+        for n in CROSSOVER_CONTEXTS:
+            if B * n > CROSSOVER_MAX_TOKENS:
+                continue
+            nb = B * n // 16
+            k = torch.randn((nb + 1, hkv, 16, d), generator=gen, device="cuda",
+                            dtype=torch.bfloat16)
+            v = torch.randn((nb + 1, hkv, 16, d), generator=gen, device="cuda",
+                            dtype=torch.bfloat16)
+            tables = torch.randperm(nb, generator=gen, device="cuda").to(torch.int32)
+            tables = tables.view(B, n // 16).contiguous()
+            ctx = torch.full((B,), n, dtype=torch.int32, device="cuda")
+            q = torch.randn((B, hq, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+            out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+            lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+            byt = B * n * 2 * hkv * d * 2
+            line = {"batch": B, "context": n, "kv_bytes": byt, "us": {}}
+            for P in CROSSOVER_PARTS:
+                if P >= n:  # one partition: the same work as P = 0
+                    continue
+                ws = torch.empty(max(1, pkv.decode_workspace_bytes(B, hq, d, n, P)),
+                                 dtype=torch.uint8, device="cuda")
+
+                def call():
+                    pkv.paged_decode(q, k, v, tables, ctx, n, partition_size=P, out=out,
+                                     lse=lse, workspace=ws)
+
+                for _ in range(3):
+                    call()
+                s_ev = torch.cuda.Event(enable_timing=True)
+                e_ev = torch.cuda.Event(enable_timing=True)
+                reps = 20
+                s_ev.record()
+                for _ in range(reps):
+                    call()
+                e_ev.record()
+                torch.cuda.synchronize()
+                line["us"][P] = round(s_ev.elapsed_time(e_ev) * 1e3 / reps, 2)
+            best = min(line["us"], key=line["us"].get)
+            line["best_partition"] = best
+            line["best_gbps"] = round(byt / line["us"][best] / 1e3, 1)
+            rows.append(line)
+            print(f"[crossover] batch {B:4d} ctx {n:6d}: " +
+                  " ".join(f"P{P}={t:.1f}" for P, t in line["us"].items()) +
+                  f"  best P{best} ({line['best_gbps']} GB/s)", file=sys.stderr, flush=True)
+            del k, v, tables, ctx, q, out, lse
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
+    return {"metric": "paged decode call time by batch x context x partition size (us)",
+            "unit": "us", "n_gpus": 1, "higher_is_better": False, "dtype": "bf16",
+            "data": "synthetic", "config": {"workload": "crossover sweep", "num_q_heads": hq,
+                                            "num_kv_heads": hkv, "head_dim": d,
+                                            "block_size": 16, "lengths": "uniform"},
+            "rows": rows}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -397,6 +476,9 @@ def main():
     import paged_kv_cache_200_amd as pkv
     from workloads import config_case, decode_step_inputs, fork_groups
 
+    if args.crossover:
+        print(json.dumps(run_crossover(args, np, torch, pkv)), flush=True)
+        return
     if args.workload == "gpt2_replay":
         print(json.dumps(run_replay(args, np, torch, pkv)), flush=True)
         return
@@ -407,10 +489,16 @@ def main():
     print(f"[bench] building inputs: {args.workload} seed {args.seed}", file=sys.stderr, flush=True)
     case = config_case(args.workload, args.seed)
     shared_path = case.fork_parent is not None and not args.no_shared_prefix
+    mfma_plain = args.decode_path == "mfma" and case.fork_parent is None
+    if mfma_plain:
+        if case.kv_dtype != "bf16":
+            print("--decode-path mfma needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        shared_path = True
     if args.partition_size is not None:
         P = args.partition_size
     else:
-        P = case.extra.get("partition_size", 1024 if shared_path else 4096)
+        P = case.extra.get("partition_size", 1024 if shared_path and not mfma_plain else 4096)
     if args.workload == "tiny":
         P = 0
     B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
@@ -436,7 +524,12 @@ def main():
     k_new, v_new = to_dev(si.k_new), to_dev(si.v_new)
     out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
-    if shared_path:
+    if mfma_plain:
+        # every sequence its own group, nothing shared: the matrix-core tile on plain decode
+        gs_np, gb_np = np.arange(B + 1, dtype=np.int32), np.zeros(B, np.int32)
+        gstarts, gblocks, max_shared = to_dev(gs_np), to_dev(gb_np), 0
+        ws_bytes = pkv.shared_prefix_workspace_bytes(B, hq, d, max_ctx, P)
+    elif shared_path:
         gs_np, gb_np = fork_groups(case)
         gstarts, gblocks, max_shared = to_dev(gs_np), to_dev(gb_np), int(gb_np.max())
         ws_bytes = pkv.shared_prefix_workspace_bytes(B, hq, d, max_ctx, P)
@@ -664,6 +757,8 @@ def main():
                      "LSE combine (one launch)"),
             "appended_tokens_per_layer": total_new,
             "launch": "hip graph of the whole step" if args.graph else "eager",
+            "decode_path": ("matrix-core tile, groups of one" if mfma_plain else
+                            "shared-prefix" if shared_path else "VALU first pass"),
             "caches": ("cold: 1 GiB read before every step" if args.cold
                        else "warm: steps back to back"),
         },

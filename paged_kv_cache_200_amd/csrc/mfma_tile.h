@@ -211,6 +211,18 @@ __device__ __forceinline__ void mfma_rows_block(MfmaRows<D>& r, MfmaBlock<D>& cu
   }
 }
 
+// A token appended in the same launch, as the tile's lanes hold it once loaded: lane
+// (c, h) keeps the K chunks of score steps k (dims 32k + 8h ..), used where c is the
+// token's slot, and the V dims c * D/16 .., used where h is its slot / 4.  The tile puts
+// them into the block holding `pos` in place of what it loaded from the cache there, so
+// the cache write of the token need not precede the tile's loads.  pos < 0: none.
+template <int D>
+struct MfmaNewToken {
+  int pos;
+  u32x4_t k[MfmaGeom<D>::kQkSteps];
+  uint32_t v[MfmaGeom<D>::kVWords];
+};
+
 // LDS of one row tile: per wave the members found not to share the leader's blocks, and
 // per wave and row the softmax state and the unnormalised output.
 template <int D>
@@ -232,15 +244,21 @@ struct MfmaShared {
 // the same loads that fetch the leader's ids).  Members that differ come back as the
 // result; if there are any, nothing is written, and the caller redoes the others
 // without them and each of them through its own row.  Called by all threads of the
-// workgroup (it synchronises).
-template <int D, int G>
+// workgroup (it synchronises).  kAgentStores: results are written with device-scope
+// stores (written through to where every XCD's device-scope loads read them), for a
+// merge by another workgroup of the same launch.  kPlain: one member (take = 1) and no
+// sharing check (member_rows unused); the query rows are then loaded by every lane (lanes
+// of rows not taken load member 0's and zero them), so no load of the tile's start is
+// conditional and the first block's loads need not wait for all earlier memory work (a
+// caller's stores included).
+template <int D, int G, bool kAgentStores = false, bool kPlain = false>
 __device__ __forceinline__ unsigned mfma_tile(
     MfmaShared<D>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ lead,
     const int32_t* __restrict__ member_rows, int W, const int (&lim)[kMfmaRows / G],
     unsigned take, int row0, int kvh, int num_q_heads, int num_kv_heads, int num_blocks,
     float scale_log2, int tok0, int slot, int slots, float* __restrict__ dst_out,
-    float* __restrict__ dst_lse) {
+    float* __restrict__ dst_lse, const MfmaNewToken<D>* nt = nullptr) {
   using Mg = MfmaGeom<D>;
   constexpr int kMembers = kMfmaRows / G;
   constexpr int kRows = kMembers * G;
@@ -265,13 +283,25 @@ __device__ __forceinline__ unsigned mfma_tile(
 
   // Query rows as the B operand of the score step (zero for rows not taken).
   u32x4_t qr[Mg::kQkSteps];
-#pragma unroll
-  for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = u32x4_t{0u, 0u, 0u, 0u};
-  if (c < kRows && ((take >> (c / G)) & 1u)) {
+  if constexpr (kPlain) {
+    const bool live = c < G;
     const uint16_t* qrow =
-        q + (static_cast<size_t>(row0 + c / G) * num_q_heads + kvh * G + c % G) * D + 8 * h;
+        q + (static_cast<size_t>(row0) * num_q_heads + kvh * G + c % G) * D + 8 * h;
 #pragma unroll
-    for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
+    for (int k = 0; k < Mg::kQkSteps; ++k) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
+      qr[k] = live ? w : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < Mg::kQkSteps; ++k) qr[k] = u32x4_t{0u, 0u, 0u, 0u};
+    if (c < kRows && ((take >> (c / G)) & 1u)) {
+      const uint16_t* qrow =
+          q + (static_cast<size_t>(row0 + c / G) * num_q_heads + kvh * G + c % G) * D + 8 * h;
+#pragma unroll
+      for (int k = 0; k < Mg::kQkSteps; ++k)
+        qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
+    }
   }
 
   MfmaRows<D> rows;
@@ -286,7 +316,7 @@ __device__ __forceinline__ unsigned mfma_tile(
     const bool live = k < nw;
     const int b = b0 + wave + kTileWaves * k;
     int id = live ? lead[b] : 0;
-    if (member_rows != nullptr) {
+    if (!kPlain && member_rows != nullptr) {
 #pragma unroll
       for (int mi = 0; mi < kMembers; ++mi) {
         const bool differs = live && ((take >> mi) & 1u) && b * kBlockTokens < lim[mi] &&
@@ -300,10 +330,10 @@ __device__ __forceinline__ unsigned mfma_tile(
     return id;
   };
   int ids = fetch_ids(0);
-  // The query loads above are conditional: without this wait the compiler cannot prove
-  // them complete at the block loop's head and waits there for every outstanding load,
-  // the block in flight included.
-  __builtin_amdgcn_s_waitcnt(0);
+  // The query loads above are conditional unless kPlain: without this wait the compiler
+  // cannot prove them complete at the block loop's head and waits there for every
+  // outstanding load, the block in flight included.
+  if constexpr (!kPlain) __builtin_amdgcn_s_waitcnt(0);
   auto load = [&](MfmaBlock<D>& bl, int k) {  // block k of the current id window
     const int id = __builtin_amdgcn_readlane(ids, k);
     const size_t off = static_cast<size_t>(id) * block_elems + kvh * head_elems;
@@ -311,6 +341,22 @@ __device__ __forceinline__ unsigned mfma_tile(
   };
   auto process = [&](MfmaBlock<D>& cur, int k) {
     const int t_base = (b0 + wave + kTileWaves * k) * kBlockTokens;  // token of slot 0
+    if constexpr (kPlain) {
+      if (nt != nullptr && nt->pos >= t_base && nt->pos < t_base + kBlockTokens) {
+        const int ts = nt->pos - t_base;
+        if (c == ts) {
+#pragma unroll
+          for (int kk = 0; kk < Mg::kQkSteps; ++kk) cur.k[kk] = nt->k[kk];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (h == ts / 4 && i == ts % 4) {
+#pragma unroll
+            for (int w = 0; w < Mg::kVWords; ++w) cur.v[i][w] = nt->v[w];
+          }
+        }
+      }
+    }
     mfma_rows_block<D>(rows, cur, qr, t_base, n_c, n_max, h, scale_log2);
   };
   // Two blocks in flight: the next block's loads are issued before this one's math.  The
@@ -395,10 +441,23 @@ __device__ __forceinline__ unsigned mfma_tile(
       }
       acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
       // dims cc * D/16 + j of tile j: float4 u holds tiles 4u .. 4u + 3
-      *reinterpret_cast<float4*>(dst + 4 * u) = acc;
+      if constexpr (kAgentStores) {
+        __hip_atomic_store(dst + 4 * u + 0, acc.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 4 * u + 1, acc.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 4 * u + 2, acc.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 4 * u + 3, acc.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *reinterpret_cast<float4*>(dst + 4 * u) = acc;
+      }
     }
-    if (cc == 0 && dst_lse != nullptr)
-      dst_lse[sh * slots + slot] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    if (cc == 0 && dst_lse != nullptr) {
+      const float ls = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      if constexpr (kAgentStores)
+        __hip_atomic_store(dst_lse + sh * slots + slot, ls, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        dst_lse[sh * slots + slot] = ls;
+    }
   }
   __syncthreads();  // LDS reused by the next call
   return differ;

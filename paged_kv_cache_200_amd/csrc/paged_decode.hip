@@ -78,8 +78,16 @@ __device__ __forceinline__ float load_partial(const float* p) {
 }
 
 // Most partial-result slots per sequence merged inside the first pass (decode_impl
-// launches the combine kernel past that).
-constexpr int kMaxInPassMergeSlots = 8;
+// launches the combine kernel past that), and the slots whose partial outputs the merging
+// workgroup loads together.
+#ifndef PKV_IN_PASS_MERGE_MAX
+#define PKV_IN_PASS_MERGE_MAX 8
+#endif
+#ifndef PKV_IN_PASS_MERGE_CHUNK
+#define PKV_IN_PASS_MERGE_CHUNK 4
+#endif
+constexpr int kMaxInPassMergeSlots = PKV_IN_PASS_MERGE_MAX;
+constexpr int kInPassMergeChunk = PKV_IN_PASS_MERGE_CHUNK;
 
 // kChunk: partitions whose partial outputs are loaded together, before their weighted
 // sum (16 in the combine kernel; 4 in the merge inside the first pass, which keeps that
@@ -91,8 +99,10 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
                                             const float* __restrict__ po, int nparts, int lane) {
   constexpr int kPer = D / kWave;  // output dims per lane
   constexpr float kLog2e = 1.44269504088896340736f;
-  float M = -INFINITY;
-  for (int p0 = 0; p0 < nparts; p0 += kWave)
+  // Up to 64 partitions the log-sum-exps are loaded once, for the max and the weights.
+  const float lp0 = lane < nparts ? load_partial<kAgent>(pl + lane) : -INFINITY;
+  float M = wave_max(lp0);
+  for (int p0 = kWave; p0 < nparts; p0 += kWave)
     M = fmaxf(M, wave_max(p0 + lane < nparts ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY));
   float acc[kPer];
 #pragma unroll
@@ -100,7 +110,7 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
   float den = 0.0f;
   for (int p0 = 0; p0 < nparts; p0 += kWave) {
     const int cnt = min(kWave, nparts - p0);
-    const float lp = lane < cnt ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY;
+    const float lp = p0 == 0 ? lp0 : lane < cnt ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY;
     const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
     den += wave_sum(w);
     int p = 0;
@@ -257,6 +267,102 @@ __device__ __forceinline__ void append_in_unit(
   }
 }
 
+// The work unit of a first-pass workgroup: which sequence, KV head and token range it
+// attends, which partial-result slot it fills (unless `direct`: its sequence's only unit,
+// written straight to out / lse), and whether its sequence is merged in this launch.
+struct Unit {
+  int part, kvh, s;  // part: the partial-result slot written unless `direct`
+  int tok0, tok1;    // the unit's token range
+  bool direct;
+  bool merge;
+};
+
+// Returns false when the workgroup has no unit (past the plan's count or the sequence's
+// partitions).
+__device__ __forceinline__ bool resolve_unit(Unit& un, int order, int num_kv_heads,
+                                             const int4* __restrict__ plan,
+                                             const int* __restrict__ plan_count,
+                                             const int32_t* __restrict__ ctx_lens, int W,
+                                             int part_tokens, const float* out,
+                                             const int* merge_ctr) {
+  const bool leader = threadIdx.x == 0;
+  un.merge = false;
+  if (order == kOrderPlanned) {
+    // The plan entry carries the unit's (range-checked) token range and slot: one load
+    // instead of dependent ones before the first block-table read.
+    const int unit = blockIdx.x / num_kv_heads;
+    un.kvh = blockIdx.x - unit * num_kv_heads;
+    if (unit >= *plan_count) return false;
+    const int4 u = plan[unit];
+    un.s = u.x;
+    un.tok0 = u.y;
+    un.tok1 = u.z;
+    un.part = u.w & kSlotMask;
+    un.direct = (u.w & kDirectFlag) != 0 && out != nullptr;
+    un.merge = !un.direct && merge_ctr != nullptr && out != nullptr;
+    return true;
+  }
+  int nx_parts;
+  if (order == kOrderPartMinor) {
+    un.part = blockIdx.x; un.kvh = blockIdx.y; un.s = blockIdx.z; nx_parts = gridDim.x;
+  } else {
+    un.kvh = blockIdx.x; un.s = blockIdx.y; un.part = gridDim.z - 1 - blockIdx.z;
+    nx_parts = gridDim.z;
+  }
+  int n = ctx_lens[un.s];
+  const int cap = W * kBlockTokens;
+  if (n < 0 || n > cap) {
+    if (leader && un.part == 0 && un.kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
+    n = n < 0 ? 0 : cap;
+  }
+  int nparts = 1;
+  un.tok0 = 0;
+  un.tok1 = n;
+  if (part_tokens > 0) {
+    nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
+    un.tok0 = un.part * part_tokens;
+    un.tok1 = min(n, un.tok0 + part_tokens);
+  }
+  if (un.part == nx_parts - 1 && nparts > nx_parts && leader && un.kvh == 0)
+    PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
+  if (un.part >= nparts) return false;
+  un.direct = nparts == 1 && out != nullptr;
+  return true;
+}
+
+// Epilogue of a split unit whose sequence is merged in this launch, after its partial
+// results were stored with device-scope stores: wait until those stores have completed,
+// take one ticket per workgroup from the (sequence, KV head) counter, and if it is the
+// last of the sequence's n_merge units, merge every slot (the log-sum-exp combine, same
+// routine and order as the combine kernel; wave w merges query heads w, w + NW, ...) and
+// reset the counter.  The counter is zeroed by the plan, so a reused plan starts from zero
+// too.  Called by all threads of the workgroup.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_when_last(int n_merge, int* __restrict__ merge_ctr, int s,
+                                                int kvh, int num_q_heads, int num_kv_heads,
+                                                int max_parts, float* __restrict__ out,
+                                                float* __restrict__ lse,
+                                                const float* __restrict__ part_out,
+                                                const float* __restrict__ part_lse, int wave,
+                                                int lane) {
+  __shared__ int s_ticket;
+  const bool leader = threadIdx.x == 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int* ctr = merge_ctr + static_cast<size_t>(s) * num_kv_heads + kvh;
+  if (leader) s_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket == n_merge - 1) {
+    for (int g = wave; g < G; g += NW) {
+      const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
+      combine_row<D, true, kInPassMergeChunk>(out + sh * D, lse != nullptr ? lse + sh : nullptr,
+                              part_lse + sh * max_parts, part_out + sh * max_parts * D, n_merge,
+                              lane);
+    }
+    if (leader) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <typename T, int D, int G>
 constexpr int pass1_min_workgroups() {
   constexpr int max_g = sizeof(T) == 2 ? (D == 64 ? 7 : 4) : (D == 64 ? 5 : 2);
@@ -273,50 +379,12 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
     const int4* __restrict__ plan, const int* __restrict__ plan_count,
     const int32_t* __restrict__ nslots, int* __restrict__ merge_ctr, const PassAppend ap) {
   using Gm = Geom<T, D>;
-  int part, kvh, s;  // part: the partial-result slot written unless `direct`
-  int tok0, tok1;    // the unit's token range
-  bool direct;       // the unit is its sequence's only one: write out / lse
-  bool merge = false;  // a split unit whose sequence is merged in this launch
-  const bool leader = threadIdx.x == 0;
-  if (order == kOrderPlanned) {
-    // The plan entry carries the unit's (range-checked) token range and slot: one load
-    // instead of dependent ones before the first block-table read.
-    const int unit = blockIdx.x / num_kv_heads;
-    kvh = blockIdx.x - unit * num_kv_heads;
-    if (unit >= *plan_count) return;
-    const int4 u = plan[unit];
-    s = u.x;
-    tok0 = u.y;
-    tok1 = u.z;
-    part = u.w & kSlotMask;
-    direct = (u.w & kDirectFlag) != 0 && out != nullptr;
-    merge = !direct && merge_ctr != nullptr && out != nullptr;
-  } else {
-    int nx_parts;
-    if (order == kOrderPartMinor) {
-      part = blockIdx.x; kvh = blockIdx.y; s = blockIdx.z; nx_parts = gridDim.x;
-    } else {
-      kvh = blockIdx.x; s = blockIdx.y; part = gridDim.z - 1 - blockIdx.z; nx_parts = gridDim.z;
-    }
-    int n = ctx_lens[s];
-    const int cap = W * kBlockTokens;
-    if (n < 0 || n > cap) {
-      if (leader && part == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CONTEXT);
-      n = n < 0 ? 0 : cap;
-    }
-    int nparts = 1;
-    tok0 = 0;
-    tok1 = n;
-    if (part_tokens > 0) {
-      nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
-      tok0 = part * part_tokens;
-      tok1 = min(n, tok0 + part_tokens);
-    }
-    if (part == nx_parts - 1 && nparts > nx_parts && leader && kvh == 0)
-      PKV_FLAG_ERROR(PKV_DEVERR_MAX_CONTEXT);
-    if (part >= nparts) return;
-    direct = nparts == 1 && out != nullptr;
-  }
+  Unit un;
+  if (!resolve_unit(un, order, num_kv_heads, plan, plan_count, ctx_lens, W, part_tokens, out,
+                    merge_ctr))
+    return;
+  const int part = un.part, kvh = un.kvh, s = un.s, tok0 = un.tok0, tok1 = un.tok1;
+  const bool direct = un.direct, merge = un.merge;
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   // (marked unlikely, which keeps the block loop's register allocation that of plain
@@ -412,28 +480,9 @@ __global__ __launch_bounds__(NW * kWave, (pass1_min_workgroups<T, D, G>())) void
     }
     // (marked unlikely: with the merge on the cold path the register allocation of the
     // block loop matches the kernel without it, which has no spill at 256 VGPRs)
-    if (__builtin_expect(n_merge > 0, 0)) {
-      // Split sequence: the last of its units to finish merges every slot (the log-sum-exp
-      // combine, same routine and order as the combine kernel).  Each thread waits until
-      // its partial stores have completed at device scope, then one ticket per workgroup
-      // is taken from the (sequence, KV head) counter.  The counter is zeroed by the plan
-      // and reset by the merging workgroup, so a reused plan starts from zero too.
-      __shared__ int s_ticket;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      int* ctr = merge_ctr + static_cast<size_t>(s) * num_kv_heads + kvh;
-      if (leader) s_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      if (s_ticket == n_merge - 1) {
-        for (int g = wave; g < G; g += NW) {
-          const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
-          combine_row<D, true, 4>(
-              out + sh * D, lse != nullptr ? lse + sh : nullptr, part_lse + sh * max_parts,
-              part_out + sh * max_parts * D, n_merge, lane);
-        }
-        if (leader) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    if (__builtin_expect(n_merge > 0, 0))
+      merge_when_last<D, G, NW>(n_merge, merge_ctr, s, kvh, num_q_heads, num_kv_heads, max_parts,
+                                out, lse, part_out, part_lse, wave, lane);
   }
 
 }
@@ -845,6 +894,153 @@ __global__ __launch_bounds__(kTileWaves * kWave) void decode_shared_mfma_kernel(
   }
 }
 
+// The first pass's in-launch append (see append_in_unit) for the matrix-core tile's lane
+// layout: a new token's K chunk of score step k (dims 32k + 8h .. + 7) is stored by lane
+// (c = slot, h), its V dims c * D/16 .. by lane (c, h = slot / 4), in the wave that takes
+// the token's block, which are the lanes that load those bytes in mfma_load_block.
+template <int D>
+__device__ __forceinline__ void mfma_append_in_unit(
+    uint16_t* kc, uint16_t* vc, const PassAppend& ap, const int32_t* __restrict__ tables, int W,
+    const int32_t* __restrict__ ctx_lens, int s, int kvh, int num_kv_heads, int num_blocks,
+    int tok0, int tok1, int wave, int lane) {
+  using Mg = MfmaGeom<D>;
+  const int c0 = ap.cu[s];
+  const int c1 = ap.cu[s + 1];
+  if (c0 < 0 || c1 < c0 || c1 > ap.total) {
+    if (wave == 0 && lane == 0 && kvh == 0) PKV_FLAG_ERROR(PKV_DEVERR_CU);
+    return;
+  }
+  const int cap = W * kBlockTokens;
+  int n = ctx_lens[s];
+  n = n < 0 ? 0 : min(n, cap);
+  const bool last_unit = tok1 >= n;
+  const int p0 = ap.start_pos[s];
+  const int b0 = tok0 / kBlockTokens;
+  const int c = lane % 16;
+  const int h = lane / 16;
+  const uint16_t* kn = static_cast<const uint16_t*>(ap.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(ap.v_new);
+  for (int t = c0; t < c1; ++t) {
+    const int pos = p0 + (t - c0);
+    const bool inside = pos >= tok0 && pos < tok1;
+    if (!inside && !(last_unit && pos >= tok1)) continue;
+    if (pos < 0 || pos >= cap) {
+      if (wave == 0 && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_POSITION);
+      continue;
+    }
+    const int bi = pos / kBlockTokens;
+    const int owner = inside ? (bi - b0) % kTileWaves : 0;
+    if (wave != owner) continue;
+    const int slot = pos % kBlockTokens;
+    const int id = tables[static_cast<size_t>(s) * W + bi];
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks)) {
+      if (lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+      continue;
+    }
+    const size_t row = ((static_cast<size_t>(id) * num_kv_heads + kvh) * kBlockTokens + slot) * D;
+    const size_t src = (static_cast<size_t>(t) * num_kv_heads + kvh) * D;
+    if (c == slot) {
+#pragma unroll
+      for (int k = 0; k < Mg::kQkSteps; ++k)
+        *reinterpret_cast<u32x4_t*>(kc + row + 32 * k + 8 * h) =
+            *reinterpret_cast<const u32x4_t*>(kn + src + 32 * k + 8 * h);
+    }
+    if (h == slot / 4) {
+      const size_t e = static_cast<size_t>(c) * Mg::kTiles;
+      if constexpr (Mg::kVWords == 4)
+        *reinterpret_cast<u32x4_t*>(vc + row + e) = *reinterpret_cast<const u32x4_t*>(vn + src + e);
+      else
+        *reinterpret_cast<u32x2_t*>(vc + row + e) = *reinterpret_cast<const u32x2_t*>(vn + src + e);
+    }
+  }
+}
+
+// Plain decode on the matrix cores, for GQA groups large enough that one 16-row tile of a
+// sequence's G query heads (the rows past G idle) costs fewer instructions per block than
+// the VALU pass's G dot products per token: one workgroup per work unit and KV head, in
+// the plan's order (or the grid orders of the first pass), with the first pass's
+// in-launch append and merge.  Results equal the first pass's within rounding (the scores
+// and the weighted sum run on the matrix cores), not bit for bit.
+template <int D, int G, bool kAppend>
+__global__ __launch_bounds__(kTileWaves * kWave) void decode_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
+    const int32_t* __restrict__ ctx_lens, int num_q_heads, int num_kv_heads, int num_blocks,
+    float scale_log2, int part_tokens, int max_parts, float* __restrict__ part_out,
+    float* __restrict__ part_lse, float* __restrict__ out, float* __restrict__ lse, int order,
+    const int4* __restrict__ plan, const int* __restrict__ plan_count,
+    const int32_t* __restrict__ nslots, int* __restrict__ merge_ctr, const PassAppend ap) {
+  __shared__ MfmaShared<D> sm;
+  Unit un;
+  if (!resolve_unit(un, order, num_kv_heads, plan, plan_count, ctx_lens, W, part_tokens, out,
+                    merge_ctr))
+    return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  uint16_t* kw = const_cast<uint16_t*>(kc);
+  uint16_t* vw = const_cast<uint16_t*>(vc);
+  // The step's new token: a sequence appending one token inside this unit's range gets it
+  // into the tile from registers (loaded now, unconditionally, from a row that is always
+  // valid) and writes the cache after the tile, so the tile's loads never wait for the
+  // write.  Several new tokens in one sequence are written before the tile and read back.
+  MfmaNewToken<D> nt;
+  nt.pos = -1;
+  bool write_first = false;
+  if constexpr (kAppend) {
+    using Mg = MfmaGeom<D>;
+    const int c0 = ap.cu[un.s];
+    const int c1 = ap.cu[un.s + 1];
+    const int p0 = ap.start_pos[un.s];
+    const int row = min(max(c0, 0), ap.total - 1);
+    const size_t src = (static_cast<size_t>(row) * num_kv_heads + un.kvh) * D;
+    const uint16_t* kn = static_cast<const uint16_t*>(ap.k_new) + src;
+    const uint16_t* vn = static_cast<const uint16_t*>(ap.v_new) + src;
+    const int c = lane % 16;
+    const int h = lane / 16;
+#pragma unroll
+    for (int k = 0; k < Mg::kQkSteps; ++k)
+      nt.k[k] = *reinterpret_cast<const u32x4_t*>(kn + 32 * k + 8 * h);
+    if constexpr (Mg::kVWords == 4) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(vn + c * Mg::kTiles);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nt.v[j] = w[j];
+    } else {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(vn + c * Mg::kTiles);
+      nt.v[0] = w[0];
+      nt.v[1] = w[1];
+    }
+    const bool valid = c0 >= 0 && c1 <= ap.total;
+    if (valid && c1 - c0 == 1 && p0 >= un.tok0 && p0 < un.tok1)
+      nt.pos = p0;
+    else
+      write_first = valid && c1 - c0 > 1;
+    if (write_first)
+      mfma_append_in_unit<D>(kw, vw, ap, tables, W, ctx_lens, un.s, un.kvh, num_kv_heads,
+                             num_blocks, un.tok0, un.tok1, wave, lane);
+  }
+  int lim[kMfmaRows / G];
+  decode_limits<G>(lim, ctx_lens, un.s, 1u, W * kBlockTokens, un.tok1);
+  // device-scope stores throughout, so that a merging workgroup of this launch reads the
+  // partial results wherever they were written
+  mfma_tile<D, G, true, true>(sm, q, kc, vc, tables + static_cast<size_t>(un.s) * W, nullptr,
+                              W, lim, 1u, un.s, un.kvh, num_q_heads, num_kv_heads, num_blocks,
+                              scale_log2, un.tok0, un.direct ? 0 : un.part,
+                              un.direct ? 1 : max_parts, un.direct ? out : part_out,
+                              un.direct ? lse : part_lse, kAppend ? &nt : nullptr);
+  if constexpr (kAppend) {
+    if (!write_first)
+      mfma_append_in_unit<D>(kw, vw, ap, tables, W, ctx_lens, un.s, un.kvh, num_kv_heads,
+                             num_blocks, un.tok0, un.tok1, wave, lane);
+  }
+  if (un.merge) {
+    const int n_merge = min(nslots[un.s], max_parts);
+    if (n_merge > 0)
+      merge_when_last<D, G, kTileWaves>(n_merge, merge_ctr, un.s, un.kvh, num_q_heads,
+                                        num_kv_heads, max_parts, out, lse, part_out, part_lse,
+                                        wave, lane);
+  }
+}
+
 using LaunchFn = void (*)(int, int, int, int, hipStream_t, const void*, const void*, const void*,
                           const int32_t*, int, const int32_t*, int, int, int, float, int, int,
                           float*, float*, float*, float*, const int4*, const int*,
@@ -885,6 +1081,31 @@ void pass1_default(int order, int np, int num_kv_heads, int batch, hipStream_t s
   pass1_launch<4, T, D, G>(order, np, num_kv_heads, batch, stream, q, kc, vc, tables, W, ctx, hq,
                            hkv, nb, scale_log2, part_tokens, max_parts, part_out, part_lse, out,
                            lse, plan, plan_count, nslots, merge_ctr, ap);
+}
+
+// The matrix-core first pass (bf16 only), in the launch shapes of pass1_launch.
+template <typename T, int D, int G>
+void mfma_pass_launch(int order, int np, int num_kv_heads, int batch, hipStream_t stream,
+                      const void* q, const void* kc, const void* vc, const int32_t* tables, int W,
+                      const int32_t* ctx, int hq, int hkv, int nb, float scale_log2,
+                      int part_tokens, int max_parts, float* part_out, float* part_lse,
+                      float* out, float* lse, const int4* plan, const int* plan_count,
+                      const int32_t* nslots, int* merge_ctr, const PassAppend& ap) {
+  static_assert(sizeof(T) == 2, "the matrix-core pass reads bf16 caches");
+  dim3 grid;
+  if (order == kOrderPlanned)
+    grid = dim3(static_cast<unsigned>(num_kv_heads) * batch * np);
+  else if (order == kOrderPartMinor)
+    grid = dim3(np, num_kv_heads, batch);
+  else
+    grid = dim3(num_kv_heads, batch, np);
+  auto kernel = ap.k_new != nullptr ? decode_mfma_kernel<D, G, true>
+                                    : decode_mfma_kernel<D, G, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kTileWaves * kWave), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                     static_cast<const uint16_t*>(vc), tables, W, ctx, hq, hkv, nb, scale_log2,
+                     part_tokens, max_parts, part_out, part_lse, out, lse, order, plan,
+                     plan_count, nslots, merge_ctr, ap);
 }
 
 struct SharedArgs {
@@ -955,17 +1176,38 @@ SharedFn pick_shared(int G) {
   }
 }
 
+// Smallest GQA group whose bf16 first pass runs on the matrix cores, per head_dim.
+#ifndef PKV_MFMA_MIN_GROUP_D64
+#define PKV_MFMA_MIN_GROUP_D64 7
+#endif
+#ifndef PKV_MFMA_MIN_GROUP_D128
+#define PKV_MFMA_MIN_GROUP_D128 7
+#endif
+
+template <typename T, int D>
+constexpr bool mfma_pass(int G) {
+  return sizeof(T) == 2 && G >= (D == 64 ? PKV_MFMA_MIN_GROUP_D64 : PKV_MFMA_MIN_GROUP_D128);
+}
+
+template <typename T, int D, int G>
+LaunchFn pass_for_group() {
+  if constexpr (mfma_pass<T, D>(G))
+    return mfma_pass_launch<T, D, G>;
+  else
+    return pass1_default<T, D, G>;
+}
+
 template <typename T, int D>
 bool pick_group(int G, LaunchFn* fn) {
   switch (G) {
-    case 1: *fn = pass1_default<T, D, 1>; return true;
-    case 2: *fn = pass1_default<T, D, 2>; return true;
-    case 3: *fn = pass1_default<T, D, 3>; return true;
-    case 4: *fn = pass1_default<T, D, 4>; return true;
-    case 5: *fn = pass1_default<T, D, 5>; return true;
-    case 6: *fn = pass1_default<T, D, 6>; return true;
-    case 7: *fn = pass1_default<T, D, 7>; return true;
-    case 8: *fn = pass1_default<T, D, 8>; return true;
+    case 1: *fn = pass_for_group<T, D, 1>(); return true;
+    case 2: *fn = pass_for_group<T, D, 2>(); return true;
+    case 3: *fn = pass_for_group<T, D, 3>(); return true;
+    case 4: *fn = pass_for_group<T, D, 4>(); return true;
+    case 5: *fn = pass_for_group<T, D, 5>(); return true;
+    case 6: *fn = pass_for_group<T, D, 6>(); return true;
+    case 7: *fn = pass_for_group<T, D, 7>(); return true;
+    case 8: *fn = pass_for_group<T, D, 8>(); return true;
     default: return false;
   }
 }
