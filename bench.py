@@ -497,8 +497,15 @@ def main():
         shared_path = True
     if args.partition_size is not None:
         P = args.partition_size
+    elif "partition_size" in case.extra:
+        P = case.extra["partition_size"]  # the workload states its own
+    elif shared_path and not mfma_plain:
+        P = 1024
     else:
-        P = case.extra.get("partition_size", 1024 if shared_path and not mfma_plain else 4096)
+        # the library's rule, from the sizes the host knows
+        P = pkv.decode_partition_size(case.batch, case.num_kv_heads, case.head_dim,
+                                      int(case.context_lens.max()),
+                                      int(case.context_lens.sum()))
     if args.workload == "tiny":
         P = 0
     B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim

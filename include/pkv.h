@@ -133,6 +133,25 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
                                   int32_t max_context_len, int32_t partition_size);
 
 /*
+ * A partition size for pkv_paged_decode and its variants, from the crossover the first
+ * pass measures on MI355X (uniform and long-tailed lengths, 1 to 256 sequences, 512 to
+ * 32768 tokens; mlsystems topic listing, flash-decoding entry: past some point, splitting
+ * the KV length beats one unit per sequence):
+ *   - 0 (one unit per sequence and KV head) when max_context_len <= 512, or when
+ *     batch * num_kv_heads >= 512 (two units per compute unit already);
+ *   - else P = the power of two in [256, 8192] at or below the call's K/V bytes divided
+ *     by 256 units (about one per compute unit), counted in tokens of a 128-dim head:
+ *     total_context_tokens * num_kv_heads * head_dim / 32768;
+ *   - raised to the smallest power of two that leaves at most 8 partitions per sequence
+ *     (merged inside the pass, no combine launch) when that at most doubles it;
+ *   - 0 when P >= max_context_len.
+ * total_context_tokens: sum of the batch's context lengths, as the host knows it; <= 0
+ * takes batch * max_context_len.  A host computation: no device access, no error.
+ */
+int32_t pkv_decode_partition_size(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len, int64_t total_context_tokens);
+
+/*
  * Work plan of the decode's first pass, written into `workspace`: the
  * (sequence, partition) units in longest-first order (every full partition,
  * then the last partition of every split sequence, so that its merge is done

@@ -36,6 +36,13 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; a ROCm installation is required to build libpkv")
 
 
+def _extra_flags():
+    """Extra hipcc flags from PKV_EXTRA_HIPCC_FLAGS, for builds of the tuning variants
+    (e.g. -DPKV_MFMA_MIN_GROUP_D64=9 -DPKV_MFMA_MIN_GROUP_D128=9: the VALU first pass for
+    every group size)."""
+    return os.environ.get("PKV_EXTRA_HIPCC_FLAGS", "").split()
+
+
 def _hip_flags():
     # -amdgpu-mfma-vgpr-form: matrix-core accumulators in ordinary VGPRs rather than AGPRs.
     # The prefill's softmax rescales its accumulators on the VALU, which cannot read AGPRs:
@@ -65,7 +72,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([hipcc, *_hip_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *_hip_flags(), *_extra_flags(), "-c", os.path.join(CSRC, src), "-o",
+                     obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-I", INCLUDE, "-c",

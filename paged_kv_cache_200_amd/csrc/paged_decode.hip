@@ -1460,6 +1460,28 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
       .bytes;
 }
 
+extern "C" int32_t pkv_decode_partition_size(int32_t batch, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_context_len,
+                                             int64_t total_context_tokens) {
+  if (batch <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 512) return 0;
+  // One unit per (sequence, KV head) already gives two workgroups per compute unit.
+  if (static_cast<int64_t>(batch) * num_kv_heads >= 512) return 0;
+  const int64_t total = total_context_tokens > 0
+                            ? total_context_tokens
+                            : static_cast<int64_t>(batch) * max_context_len;
+  // The pass's bytes spread over about one unit per compute unit, counted in tokens of a
+  // 128-dim head: a power of two in [256, 8192].
+  const int64_t share = total * num_kv_heads * head_dim / (256 * 128);
+  int32_t P = 256;
+  while (P < 8192 && 2 * static_cast<int64_t>(P) <= share) P *= 2;
+  // Few enough partitions to merge inside the pass, if that costs at most one doubling.
+  const int32_t per_merge = (max_context_len + kMaxInPassMergeSlots - 1) / kMaxInPassMergeSlots;
+  int32_t merge_p = kBlockTokens;
+  while (merge_p < per_merge) merge_p *= 2;
+  if (merge_p <= 2 * P) P = min(max(P, merge_p), 8192);
+  return P >= max_context_len ? 0 : P;
+}
+
 extern "C" size_t pkv_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                                     int32_t head_dim, int32_t max_context_len,
                                                     int32_t partition_size) {

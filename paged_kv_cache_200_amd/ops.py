@@ -105,6 +105,16 @@ def decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, partit
                                                      max_context_len, partition_size))
 
 
+def decode_partition_size(batch, num_kv_heads, head_dim, max_context_len,
+                          total_context_tokens=0) -> int:
+    """The library's partition-size rule (pkv_decode_partition_size): 0 (no split) or a
+    power of two from the call's size; total_context_tokens <= 0 assumes every sequence
+    is max_context_len long."""
+    return int(_lib.lib().pkv_decode_partition_size(batch, num_kv_heads, head_dim,
+                                                    int(max_context_len),
+                                                    int(total_context_tokens)))
+
+
 def shared_prefix_workspace_bytes(batch, num_q_heads, head_dim, max_context_len,
                                   partition_size) -> int:
     return int(_lib.lib().pkv_shared_prefix_workspace_bytes(batch, num_q_heads, head_dim,
@@ -315,15 +325,22 @@ class DecodeStep:
     (a single launch while no sequence has more than IN_PASS_MERGE_MAX_PARTITIONS
     partitions), with the same results as the function.
 
+    partition_size None (the default) takes the library's rule (decode_partition_size),
+    from max_context_len and, when given, the step's total_context_tokens.
+
     Bound tensors must stay allocated and keep their shapes while the object is used.
     Their contents may change in place between steps; plan() must then run again before
     the next layer().  Results go to the bound out/lse unless a layer passes its own.
     """
 
     def __init__(self, q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
-                 cu_new_tokens, context_lens, max_context_len, scale=None, partition_size=0,
-                 out=None, lse=None, want_lse=True, workspace=None, stream=None, plan=True):
+                 cu_new_tokens, context_lens, max_context_len, scale=None, partition_size=None,
+                 out=None, lse=None, want_lse=True, workspace=None, stream=None, plan=True,
+                 total_context_tokens=0):
         B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens)
+        if partition_size is None:
+            partition_size = decode_partition_size(B, hkv, d, max_context_len,
+                                                   total_context_tokens)
         _append_checks(k_cache, k_new, v_new, start_pos, cu_new_tokens, B, hkv, d)
         if scale is None:
             scale = 1.0 / math.sqrt(d)

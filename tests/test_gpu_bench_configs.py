@@ -1,5 +1,6 @@
 """The exact library calls bench.py times, at the workloads' full sizes, against the oracle:
-the 256-sequence decode step (append + decode in one call, partition 4096), the
+the 256-sequence decode step (append + decode in one call, at the library's partition-size
+rule and at partition 4096), the
 copy-on-write fork step (append + shared-prefix decode, partition 1024) and the chunked
 prefill (every sequence, sampled query rows)."""
 
@@ -31,18 +32,21 @@ def _oracle_step(case, si):
                            case.kv_dtype)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_high_concurrency_step_as_benched(seed):
-    """Seeds 0-2: seed 1 holds an 8192-token sequence, exactly two full partitions."""
+@pytest.mark.parametrize("seed,rule", [(0, True), (1, True), (2, True), (0, False), (1, False)])
+def test_high_concurrency_step_as_benched(seed, rule):
+    """Seeds 0-2 at the rule's partition size; at 4096, seed 1 holds an 8192-token
+    sequence, exactly two full partitions."""
     import paged_kv_cache_200_amd as pkv
-    say(f"bench config: high_concurrency seed {seed}, append_paged_decode, P=4096")
     case = config_case("high_concurrency", seed)
+    P = (pkv.decode_partition_size(case.batch, 8, 128, int(case.context_lens.max()),
+                                   int(case.context_lens.sum())) if rule else 4096)
+    say(f"bench config: high_concurrency seed {seed}, append_paged_decode, P={P}")
     si = decode_step_inputs(case, seed)
     k, v = dev(case.k_pool[0]), dev(case.v_pool[0])
     o, l = pkv.append_paged_decode(dev(case.q[0]), k, v, dev(si.k_new), dev(si.v_new),
                                    dev(case.block_tables), dev(si.start_pos), dev(si.cu_new),
                                    dev(case.context_lens), int(case.context_lens.max()),
-                                   scale=float(case.scale), partition_size=4096)
+                                   scale=float(case.scale), partition_size=P)
     torch.cuda.synchronize()
     kp, vp = pa.kv_append(case.k_pool[0], case.v_pool[0], si.k_new, si.v_new,
                           case.block_tables, si.start_pos, si.cu_new)
@@ -51,7 +55,7 @@ def test_high_concurrency_step_as_benched(seed):
     assert_parity((o.cpu().numpy(), l.cpu().numpy()),
                   pa.paged_decode(case.q[0], kp, vp, case.block_tables, case.context_lens,
                                   case.scale, case.kv_dtype),
-                  "bf16", f"high_concurrency s{seed} as benched")
+                  "bf16", f"high_concurrency s{seed} P{P} as benched")
     assert_no_device_error()
 
 

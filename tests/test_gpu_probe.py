@@ -206,14 +206,19 @@ def test_probe_long_context(P):
     _probe_decode(case, paths, P, seed=11, what="long_context")
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_probe_high_concurrency_as_benched(seed):
-    """The benched call (append + decode, partition 4096) on the full 256-sequence
-    workload of each seed; seed 0 also through the in-pass append that DecodeStep uses."""
-    say(f"probe high_concurrency seed {seed}")
+@pytest.mark.parametrize("seed,rule", [(0, True), (1, True), (2, True), (0, False)])
+def test_probe_high_concurrency_as_benched(seed, rule):
+    """The benched call (append + decode at the library's partition-size rule, which is
+    no split here) on the full 256-sequence workload of each seed; seed 0 also through the
+    in-pass append that DecodeStep uses, and at partition 4096 (split, merged in the
+    pass)."""
+    from paged_kv_cache_200_amd import ops
     case = config_case("high_concurrency", seed)
+    P = (ops.decode_partition_size(case.batch, 8, 128, int(case.context_lens.max()),
+                                   int(case.context_lens.sum())) if rule else 4096)
+    say(f"probe high_concurrency seed {seed} P{P}")
     paths = ["append", "in_pass"] if seed == 0 else ["append"]
-    _probe_decode(case, paths, 4096, seed=seed, what=f"high_concurrency s{seed}")
+    _probe_decode(case, paths, P, seed=seed, what=f"high_concurrency s{seed}")
 
 
 @pytest.mark.parametrize("P", [512, 0])

@@ -334,8 +334,7 @@ CONFIGS = {
     # GPT-2 124M replay, fp32, 12 layers, 24 sequences, 8192-token pool
     "gpt2_replay": dict(kv_dtype="f32", hq=12, hkv=12, d=64, batch=24, layers=12),
     # Qwen2.5-0.5B attention shape, bf16 K/V, 14 q heads over 2 KV heads, 24 layers
-    "qwen_gqa": dict(kv_dtype="bf16", hq=14, hkv=2, d=64, batch=64, layers=24,
-                     partition_size=512),
+    "qwen_gqa": dict(kv_dtype="bf16", hq=14, hkv=2, d=64, batch=64, layers=24),
     # bandwidth-bound decode, bf16, 32 q heads over 8 KV heads, head_dim 128, 256 seqs
     "high_concurrency": dict(kv_dtype="bf16", hq=32, hkv=8, d=128, batch=256, layers=1),
     # 16 parents x 2048-token prefix, forked 4 ways, plus 0..256 private tokens
