@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["paged_decode.hip", "prefill.hip", "kv_append.hip", "copy_blocks.hip",
-               "status.hip"]
+               "status.hip", "static_scratch.hip"]
 HOST_SOURCES = ["block_manager.cpp", "replay.cpp"]
 
 
