@@ -143,13 +143,20 @@ __device__ __forceinline__ void stage_read_tr(TrBlock<D>& b, const LdsStage<D>& 
   }
 }
 
-// mfma_rows_block on a transpose-read block: the same scores, softmax and two-term P, with
-// output tile j holding dims 16j + c.
+// One block for a wave's 16 rows on a transpose-read block: scores as in mfma_rows_block,
+// then P rounded once to bf16 (round to nearest even, two values per v_cvt_pk_bf16_f32) as
+// the A operand of a 16x16x16 product per output tile, whose B operand is the transposed
+// V pair as read (output tile j holds dims 16j + c).  kMasked: some row's causal limit or
+// the chunk's end falls inside the block, so scores are masked per row; blocks below every
+// row's limit skip the compares.
+typedef short v4i16_t2 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
+
 template <int D>
 __device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
                                               const u32x4_t (&qr)[MfmaGeom<D>::kQkSteps],
                                               int t_base, int n_c, int n_max, int h,
-                                              float scale_log2) {
+                                              float scale_log2, bool masked) {
   using Mg = MfmaGeom<D>;
   f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -158,12 +165,13 @@ __device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
                                                  __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
                                                  0);
   float x[4];
-  float bm = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = (t_base + 4 * h + i < n_c) ? sc[i] * scale_log2 : -INFINITY;
-    bm = fmaxf(bm, x[i]);
+  for (int i = 0; i < 4; ++i) x[i] = sc[i] * scale_log2;
+  if (masked) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (t_base + 4 * h + i < n_c) ? x[i] : -INFINITY;
   }
+  float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   bm = max_xor32(max_xor16(bm));
   const bool raise = bm > r.m_c + kLazyMaxSlack;
   if (__any(raise)) {
@@ -190,17 +198,13 @@ __device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
     p[i] = fast_exp2(x[i] - r.m_c);
     r.l_part += p[i];
   }
-  uint32_t pw[4], rw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pw[i] = __float_as_uint(p[i]);
-    rw[i] = __float_as_uint(p[i] - __uint_as_float(pw[i] & 0xffff0000u));
-  }
-  const bf16x8_t a = __builtin_bit_cast(
-      bf16x8_t, u32x4_t{__builtin_amdgcn_perm(pw[1], pw[0], kHighHalves),
-                        __builtin_amdgcn_perm(pw[3], pw[2], kHighHalves),
-                        __builtin_amdgcn_perm(rw[1], rw[0], kHighHalves),
-                        __builtin_amdgcn_perm(rw[3], rw[2], kHighHalves)});
+  bf16x2_t2 p01, p23;
+  p01[0] = static_cast<__bf16>(p[0]);
+  p01[1] = static_cast<__bf16>(p[1]);
+  p23[0] = static_cast<__bf16>(p[2]);
+  p23[1] = static_cast<__bf16>(p[3]);
+  const v4i16_t2 a = __builtin_bit_cast(
+      v4i16_t2, u32x2_t{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)});
   // Tokens past every taken row's end hold stale data: zero their V (0 * NaN); word 0 holds
   // tokens 4h, 4h + 1 (low, high half), word 1 tokens 4h + 2, 4h + 3.
   if (t_base + kBlockTokens > n_max) {
@@ -213,14 +217,10 @@ __device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
       cur.vt[j][1] &= m1;
     }
   }
-  // P V: the 32-long k of the 16x16x32 product runs over (term, token), lane (c, h) giving
-  // P_hi[c][4h .. 4h + 3] then P_lo[c][4h .. 4h + 3]; the B operand is V[4h .. 4h + 3] twice.
 #pragma unroll
-  for (int j = 0; j < Mg::kTiles; ++j) {
-    const bf16x8_t b = __builtin_bit_cast(
-        bf16x8_t, u32x4_t{cur.vt[j][0], cur.vt[j][1], cur.vt[j][0], cur.vt[j][1]});
-    r.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, r.o[j], 0, 0, 0);
-  }
+  for (int j = 0; j < Mg::kTiles; ++j)
+    r.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(v4i16_t2, cur.vt[j]),
+                                                       r.o[j], 0, 0, 0);
 }
 
 template <int D, int G, int kR>
@@ -256,6 +256,7 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
 
   // This wave's row tiles: tokens tg + (wave * kR + r) * kMembers + c / G.
   int n_c[kR], members[kR], tile_end[kR];
+  int tile_lim0[kR];  // the smallest causal limit of the tile's rows (its first token's)
   int n_wave = 0;
   u32x4_t qr[kR][Mg::kQkSteps];
   MfmaRows<D> rows[kR];
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
     const bool live = c < kRows && c / G < members[r];
     n_c[r] = live ? pos0 + c / G + 1 : 0;
     tile_end[r] = members[r] > 0 ? pos0 + members[r] : 0;
+    tile_lim0[r] = pos0 + 1;
     n_wave = max(n_wave, tile_end[r]);
 #pragma unroll
     for (int k = 0; k < Mg::kQkSteps; ++k) qr[r][k] = u32x4_t{0u, 0u, 0u, 0u};
@@ -307,7 +309,8 @@ __global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
 #pragma unroll
     for (int r = 0; r < kR; ++r)
       if (t_base < tile_end[r])
-        tr_rows_block<D>(rows[r], cur, qr[r], t_base, n_c[r], n_wave, h, scale_log2);
+        tr_rows_block<D>(rows[r], cur, qr[r], t_base, n_c[r], n_wave, h, scale_log2,
+                         t_base + kBlockTokens > tile_lim0[r]);
   };
 
   // Three LDS stages, three register sets: the loads of block j are issued two blocks
