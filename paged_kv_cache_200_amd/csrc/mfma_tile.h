@@ -28,6 +28,11 @@ constexpr int kTileWaves = 4;  // waves of a tile workgroup
 //     c * D/16 .. of 4 tokens.
 //   O tile j: lane holds rows 4h + r, dim c * D/16 + j.
 constexpr int kMfmaRows = 16;
+// Blocks in flight per wave in the plain-decode tile.
+#ifndef PKV_MFMA_PLAIN_DEPTH
+#define PKV_MFMA_PLAIN_DEPTH 4
+#endif
+constexpr int kPlainDepth = PKV_MFMA_PLAIN_DEPTH;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -363,24 +368,45 @@ __device__ __forceinline__ unsigned mfma_tile(
   // loads of the steady loop are unconditional (a conditional one would make the
   // compiler's wait before the math cover the block in flight too); each window of 64
   // blocks, one id per lane, is streamed on its own.
-  MfmaBlock<D> bufa, bufb;
-  for (int wb = 0; wb < nw; wb += kWave) {
-    if (wb > 0) ids = fetch_ids(wb);
-    const int n = min(kWave, nw - wb);
-    load(bufa, 0);
-    int k = 0;  // window block k is in bufa
-    for (; k + 2 < n; k += 2) {
-      load(bufb, k + 1);
-      process(bufa, wb + k);
-      load(bufa, k + 2);
-      process(bufb, wb + k + 1);
+  if constexpr (kPlain) {
+    // A plain decode unit is a short chain of blocks per wave (8 for 512 tokens): keep
+    // kPlainDepth of them in flight.  Loads past the window's last block load that block
+    // again (a cache hit, never processed), so every load is unconditional; only the
+    // processing of those slots is skipped.
+    MfmaBlock<D> buf[kPlainDepth];
+    for (int wb = 0; wb < nw; wb += kWave) {
+      if (wb > 0) ids = fetch_ids(wb);
+      const int n = min(kWave, nw - wb);
+#pragma unroll
+      for (int i = 0; i < kPlainDepth - 1; ++i) load(buf[i], min(i, n - 1));
+      for (int k = 0; k < n; k += kPlainDepth) {
+#pragma unroll
+        for (int u = 0; u < kPlainDepth; ++u) {
+          load(buf[(u + kPlainDepth - 1) % kPlainDepth], min(k + u + kPlainDepth - 1, n - 1));
+          if (k + u < n) process(buf[u], wb + k + u);
+        }
+      }
     }
-    if (n - k == 2) {
-      load(bufb, k + 1);
-      process(bufa, wb + k);
-      process(bufb, wb + k + 1);
-    } else {
-      process(bufa, wb + k);
+  } else {
+    MfmaBlock<D> bufa, bufb;
+    for (int wb = 0; wb < nw; wb += kWave) {
+      if (wb > 0) ids = fetch_ids(wb);
+      const int n = min(kWave, nw - wb);
+      load(bufa, 0);
+      int k = 0;  // window block k is in bufa
+      for (; k + 2 < n; k += 2) {
+        load(bufb, k + 1);
+        process(bufa, wb + k);
+        load(bufa, k + 2);
+        process(bufb, wb + k + 1);
+      }
+      if (n - k == 2) {
+        load(bufb, k + 1);
+        process(bufa, wb + k);
+        process(bufb, wb + k + 1);
+      } else {
+        process(bufa, wb + k);
+      }
     }
   }
   float l_c = rows.l_part;

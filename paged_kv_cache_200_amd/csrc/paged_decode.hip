@@ -82,16 +82,16 @@ __device__ __forceinline__ float load_partial(const float* p) {
 #define PKV_IN_PASS_MERGE_MAX 8
 #endif
 #ifndef PKV_IN_PASS_MERGE_CHUNK
-#define PKV_IN_PASS_MERGE_CHUNK 4
+#define PKV_IN_PASS_MERGE_CHUNK 8
 #endif
 constexpr int kMaxInPassMergeSlots = PKV_IN_PASS_MERGE_MAX;
 constexpr int kInPassMergeChunk = PKV_IN_PASS_MERGE_CHUNK;
 
 // kChunk: partitions whose partial outputs are loaded together, before their weighted
-// sum (16 in the combine kernel; 4 in the merge inside the first pass, which keeps that
-// kernel's register allocation).  The sum runs over the partitions in order whatever the
-// chunk, so both give the same bits.
-template <int D, bool kAgent = false, int kChunk = 16>
+// sum (32 in the combine kernel; 8 in the merge inside the first pass).  The sum runs over
+// the partitions in order whatever the chunk (a chunk's slots past the last partition add
+// 0), so both give the same bits.
+template <int D, bool kAgent = false, int kChunk = 32>
 __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* __restrict__ lse_el,
                                             const float* __restrict__ pl,
                                             const float* __restrict__ po, int nparts, int lane) {
@@ -111,27 +111,23 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
     const float lp = p0 == 0 ? lp0 : lane < cnt ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY;
     const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
     den += wave_sum(w);
-    int p = 0;
-    for (; p + kChunk <= cnt; p += kChunk) {
+    // kChunk partitions' loads in flight at a time; past the last partition the weight is
+    // 0 and nothing is loaded, so the step adds 0 (every chunk is whole, no serial tail)
+    for (int p = 0; p < cnt; p += kChunk) {
       float wp[kChunk];
       float x[kChunk][kPer];
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
-        wp[u] = __shfl(w, p + u);
+        const bool live = p + u < cnt;
+        wp[u] = __shfl(w, (p + u) % kWave);
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-          x[u][j] = load_partial<kAgent>(po + (p0 + p + u) * D + j * kWave + lane);
+          x[u][j] = live ? load_partial<kAgent>(po + (p0 + p + u) * D + j * kWave + lane) : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < kChunk; ++u)
 #pragma unroll
         for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp[u], x[u][j], acc[j]);
-    }
-    for (; p < cnt; ++p) {
-      const float wp = __shfl(w, p);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        acc[j] = fmaf(wp, load_partial<kAgent>(po + (p0 + p) * D + j * kWave + lane), acc[j]);
     }
   }
 #pragma unroll

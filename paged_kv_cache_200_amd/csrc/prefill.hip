@@ -223,8 +223,15 @@ __device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
                                                        r.o[j], 0, 0, 0);
 }
 
+// Row tiles per wave of the bf16 prefill (each LDS read of a block serves kR tiles), and
+// workgroups per compute unit the register allocation is held to.
+#ifndef PKV_PREFILL_ROW_TILES
+#define PKV_PREFILL_ROW_TILES 1
+#endif
+constexpr int kPrefillRowTiles = PKV_PREFILL_ROW_TILES;
+
 template <int D, int G, int kR>
-__global__ __launch_bounds__(kLdsThreads, 4) void prefill_lds_kernel(
+__global__ __launch_bounds__(kLdsThreads, kR == 1 ? 4 : 2) void prefill_lds_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens, int total_q,
@@ -443,7 +450,7 @@ struct PrefillArgs {
 template <typename T, int D, int G>
 void prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    constexpr int kR = 1;
+    constexpr int kR = kPrefillRowTiles;
     constexpr int kGroupTokens = kMfmaRows / G * kR * kLdsWaves;
     const dim3 grid((a.max_q_len + kGroupTokens - 1) / kGroupTokens, a.batch, a.hkv);
     hipLaunchKernelGGL((prefill_lds_kernel<D, G, kR>), grid, dim3(kLdsThreads), 0, stream,
