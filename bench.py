@@ -327,17 +327,25 @@ def run_replay(args, np, torch, pkv):
     ws = torch.empty(pkv.decode_workspace_bytes(B, hq, d, 320, 0), dtype=torch.uint8,
                      device="cuda")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    seq_ids = np.asarray(ids, np.int32)
+    prompt = np.asarray(sched.prompt_lens, np.int32)
+    gen = np.asarray(sched.gen_lens, np.int32)
+    ones = np.ones(B, np.int32)
+    # one host buffer per step: tables [n, W], start [n], ctx [n], cu [n + 1]
+    host = np.empty(B * W + 3 * B + 1, np.int32)
     t0 = time.perf_counter()
     ev0.record()
     for t in range(steps):
         active = plan[t]
-        pos = np.array([int(sched.prompt_lens[s]) + t for s in active], np.int32)
-        for s, p_ in zip(active, pos):
-            bm.prepare_write(ids[s], int(p_), 1)
         n = len(active)
-        host = np.concatenate([bm.tables([ids[s] for s in active], W).reshape(-1), pos, pos + 1,
-                               np.arange(n + 1, dtype=np.int32)])
-        dev_all = torch.from_numpy(host).cuda()
+        act = np.asarray(active, np.intp)
+        pos = prompt[act] + t
+        # every sequence's next slot made writable and the tables written in one call
+        bm.prepare_step(seq_ids[act], pos, ones[:n], W, tables_out=host[:n * W].reshape(n, W))
+        host[n * W:n * W + n] = pos
+        host[n * W + n:n * W + 2 * n] = pos + 1
+        host[n * W + 2 * n:n * W + 3 * n + 1] = np.arange(n + 1, dtype=np.int32)
+        dev_all = torch.from_numpy(host[:n * W + 3 * n + 1]).cuda()
         d_tables = dev_all[:n * W].view(n, W)
         d_start = dev_all[n * W:n * W + n]
         d_ctx = dev_all[n * W + n:n * W + 2 * n]
@@ -355,9 +363,8 @@ def run_replay(args, np, torch, pkv):
         total_tokens += L * int(ctxs.sum())
         total_bytes += L * (int(ctxs.sum()) * 2 * hkv * d * 4 + n * (hq * d * 4 * 2 + 4) +
                             int(((ctxs + 15) // 16).sum()) * 4 + n * (2 * 2 * hkv * d * 4 + 12))
-        for s in active:
-            if t == int(sched.gen_lens[s]) - 1:
-                bm.free_sequence(ids[s])
+        for s in act[gen[act] == t + 1]:
+            bm.free_sequence(ids[s])
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -55,6 +55,20 @@ int pkv_bm_add_sequence(pkv_bm* bm, int32_t* seq_out);
 int pkv_bm_prepare_write(pkv_bm* bm, int32_t seq, int32_t start, int32_t n, int32_t* copy_src,
                          int32_t* copy_dst, int32_t copy_cap, int32_t* n_copies);
 
+/*
+ * One decode step's bookkeeping in one call: pkv_bm_prepare_write(seqs[r],
+ * starts[r], counts[r]) for r = 0 .. nseq-1 in order, the copies of all of them
+ * appended to copy_src/copy_dst (capacity copy_cap in total), then (tables not
+ * NULL) pkv_bm_fill_tables(seqs, nseq, tables, width, pad_id).  *n_done counts
+ * the sequences prepared; on an error (PKV_ERR_OUT_OF_BLOCKS included) the
+ * first *n_done writes stay done, sequence *n_done is unchanged and the rest
+ * are not attempted, and the tables are not filled.
+ */
+int pkv_bm_prepare_step(pkv_bm* bm, const int32_t* seqs, const int32_t* starts,
+                        const int32_t* counts, int32_t nseq, int32_t* tables, int32_t width,
+                        int32_t pad_id, int32_t* copy_src, int32_t* copy_dst, int32_t copy_cap,
+                        int32_t* n_copies, int32_t* n_done);
+
 /* New sequence sharing every block of `parent`; each shared block's count +1. */
 int pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t* child_out);
 

@@ -92,6 +92,8 @@ SIGNATURES = {
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_add_sequence": (ctypes.c_int, [_vp, _pi32]),
     "pkv_bm_prepare_write": (ctypes.c_int, [_vp, _i32, _i32, _i32, _pi32, _pi32, _i32, _pi32]),
+    "pkv_bm_prepare_step": (ctypes.c_int, [_vp, _pi32, _pi32, _pi32, _i32, _pi32, _i32, _i32,
+                                           _pi32, _pi32, _i32, _pi32, _pi32]),
     "pkv_bm_fork": (ctypes.c_int, [_vp, _i32, _pi32]),
     "pkv_bm_free_sequence": (ctypes.c_int, [_vp, _i32]),
     "pkv_bm_num_blocks_of": (ctypes.c_int, [_vp, _i32, _pi32]),

@@ -60,6 +60,32 @@ class BlockManager:
         _lib.check("pkv_bm_prepare_write", st)
         return [(int(a), int(b)) for a, b in zip(src[:cnt.value], dst[:cnt.value])]
 
+    def prepare_step(self, seqs, starts, counts, width: int, pad_id: int = 0,
+                     tables_out: np.ndarray | None = None):
+        """One step's writes and tables in one native call: prepare_write(seqs[r], starts[r],
+        counts[r]) for every r in order, then the dense int32 [len(seqs), width] tables
+        (into tables_out when given).  Returns (tables, [(src, dst), ...] copies).  On an
+        exhausted pool raises OutOfBlocks; the writes before the failing sequence stay done."""
+        s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+        st_ = np.ascontiguousarray(np.asarray(starts, np.int32))
+        ct = np.ascontiguousarray(np.asarray(counts, np.int32))
+        n = len(s)
+        out = tables_out if tables_out is not None else np.empty((n, width), np.int32)
+        if out.shape != (n, width) or out.dtype != np.int32 or not out.flags.c_contiguous:
+            raise ValueError("tables_out must be a contiguous int32 [len(seqs), width] array")
+        cap = int(ct.sum()) // self.block_size + 2 * n + 1
+        src = np.zeros(cap, np.int32)
+        dst = np.zeros(cap, np.int32)
+        cnt, done = ctypes.c_int32(), ctypes.c_int32()
+        st = self._lib.pkv_bm_prepare_step(self._h, _i32p(s), _i32p(st_), _i32p(ct), n,
+                                           _i32p(out), int(width), int(pad_id), _i32p(src),
+                                           _i32p(dst), cap, ctypes.byref(cnt),
+                                           ctypes.byref(done))
+        if st == _lib.PKV_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(f"block pool exhausted at sequence {s[done.value]}")
+        _lib.check("pkv_bm_prepare_step", st)
+        return out, [(int(a), int(b)) for a, b in zip(src[:cnt.value], dst[:cnt.value])]
+
     def fork(self, parent: int) -> int:
         out = ctypes.c_int32()
         _lib.call("pkv_bm_fork", self._h, int(parent), ctypes.byref(out))

@@ -124,6 +124,28 @@ extern "C" int pkv_bm_prepare_write(pkv_bm* bm, int32_t seq, int32_t start, int3
   return PKV_OK;
 }
 
+extern "C" int pkv_bm_prepare_step(pkv_bm* bm, const int32_t* seqs, const int32_t* starts,
+                                   const int32_t* counts, int32_t nseq, int32_t* tables,
+                                   int32_t width, int32_t pad_id, int32_t* copy_src,
+                                   int32_t* copy_dst, int32_t copy_cap, int32_t* n_copies,
+                                   int32_t* n_done) {
+  if (!bm || !seqs || !starts || !counts || !n_copies || !n_done) return PKV_ERR_NULL;
+  if (nseq < 0 || copy_cap < 0) return PKV_ERR_ARG;
+  *n_copies = 0;
+  *n_done = 0;
+  for (int32_t r = 0; r < nseq; ++r) {
+    int32_t k = 0;
+    const int st = pkv_bm_prepare_write(bm, seqs[r], starts[r], counts[r],
+                                        copy_src ? copy_src + *n_copies : nullptr,
+                                        copy_dst ? copy_dst + *n_copies : nullptr,
+                                        copy_cap - *n_copies, &k);
+    if (st != PKV_OK) return st;
+    *n_copies += k;
+    *n_done = r + 1;
+  }
+  return tables ? pkv_bm_fill_tables(bm, seqs, nseq, tables, width, pad_id) : PKV_OK;
+}
+
 extern "C" int pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t* child_out) {
   if (!bm || !child_out) return PKV_ERR_NULL;
   const std::vector<int32_t>* ptable = find_table(bm, parent);

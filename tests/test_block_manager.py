@@ -94,3 +94,39 @@ def test_errors(bm_mod):
         bm_mod.BlockManager(3, 16, free_order=[0, 0, 1])
     t = bm.tables([s], 3, pad_id=7)
     assert t.tolist() == [[7, 7, 7]]
+
+
+def test_prepare_step_equals_one_call_per_sequence(bm_mod):
+    """pkv_bm_prepare_step: the writes of a step in one call give the tables, copies and
+    free list of one prepare_write per sequence in the same order, then fill_tables."""
+    rng = np.random.default_rng(5)
+    order = rng.permutation(96).astype(np.int32)
+    one, batched = bm_mod.BlockManager(96, 16, order), bm_mod.BlockManager(96, 16, order)
+    seqs = [one.add_sequence() for _ in range(6)]
+    assert [batched.add_sequence() for _ in range(6)] == seqs
+    pos = [0] * 6
+    for step in range(40):
+        if step == 7:  # forks share blocks: the next writes copy them
+            for b in (one, batched):
+                b.fork(seqs[0])
+            seqs.append(6)
+            pos.append(pos[0])
+        counts = [int(rng.integers(0, 20)) if step % 9 == 0 else 1 for _ in seqs]
+        copies = []
+        for s, p, c in zip(seqs, pos, counts):
+            copies += one.prepare_write(s, p, c)
+        want = one.tables(seqs, 40, pad_id=-1)
+        got, got_copies = batched.prepare_step(seqs, pos, counts, 40, pad_id=-1)
+        assert np.array_equal(got, want) and got_copies == copies
+        assert batched.free_list() == one.free_list()
+        pos = [p + c for p, c in zip(pos, counts)]
+
+
+def test_prepare_step_stops_at_an_exhausted_pool(bm_mod):
+    bm = bm_mod.BlockManager(4, 16)
+    a, b, c = bm.add_sequence(), bm.add_sequence(), bm.add_sequence()
+    with pytest.raises(bm_mod.OutOfBlocks):
+        bm.prepare_step([a, b, c], [0, 0, 0], [32, 16, 32], 4)
+    # a and b were written, c (which needed 2 blocks with 1 left) was not touched
+    assert len(bm.table(a)) == 2 and len(bm.table(b)) == 1 and bm.table(c) == []
+    assert bm.num_free() == 1
