@@ -37,7 +37,8 @@ TRAFFIC_FILES = {w: os.path.join(ROOT, "profiles", f"traffic_{w}.json")
 # the sources that define the first pass (and the plan/append prologue of its step);
 # counters taken on other sources are not reported
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_200_amd", "csrc", f)
-               for f in ("paged_decode.hip", "common.h", "append_row.h", "valu_attend.h")]
+               for f in ("paged_decode.hip", "common.h", "append_row.h", "valu_attend.h",
+                         "mfma_tile.h")]
 
 
 def decode_source_digest():
@@ -661,7 +662,9 @@ def main():
     # is timed without it
     plan_ws = pkv.decode_plan(ctx, tables, hq, d, max_ctx, P)
     np_max = max(1, -(-max_ctx // P)) if P > 0 else 1
-    timed_kernel = "decode_pass1_kernel"
+    timed_kernel = ("decode_mfma_kernel"
+                    if pkv.decode_engine(case.kv_dtype, d, hq, hkv) == "matrix"
+                    else "decode_pass1_kernel")
     if shared_path:
         # no single dominant kernel: the whole decode call (plan, shared-prefix pass, first
         # pass over the private ranges, combine) against the unique bytes
@@ -772,7 +775,9 @@ def main():
             "appended_tokens_per_layer": total_new,
             "launch": "hip graph of the whole step" if args.graph else "eager",
             "decode_path": ("matrix-core tile, groups of one" if mfma_plain else
-                            "shared-prefix" if shared_path else "VALU first pass"),
+                            "shared-prefix" if shared_path else
+                            "matrix-core first pass" if timed_kernel == "decode_mfma_kernel"
+                            else "VALU first pass"),
             "caches": ("cold: 1 GiB read before every step" if args.cold
                        else "warm: steps back to back"),
         },

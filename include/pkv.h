@@ -152,6 +152,19 @@ int32_t pkv_decode_partition_size(int32_t batch, int32_t num_kv_heads, int32_t h
                                   int32_t max_context_len, int64_t total_context_tokens);
 
 /*
+ * Which engine runs the first pass of pkv_paged_decode and its variants for these
+ * shapes: PKV_ENGINE_VALU (the vector-ALU pass, decode_pass1_kernel) or
+ * PKV_ENGINE_MATRIX (the bf16 matrix-core tile, decode_mfma_kernel, used when a KV
+ * head serves 7 or 8 query heads).  Both compute the same attention; the choice
+ * follows a measured sweep over group sizes on MI355X.  A host computation:
+ * PKV_ERR_DTYPE or PKV_ERR_SHAPE for shapes the decode calls refuse.
+ */
+#define PKV_ENGINE_VALU 0
+#define PKV_ENGINE_MATRIX 1
+int32_t pkv_decode_engine(int32_t kv_dtype, int32_t head_dim, int32_t num_q_heads,
+                          int32_t num_kv_heads);
+
+/*
  * Work plan of the decode's first pass, written into `workspace`: the
  * (sequence, partition) units in longest-first order (every full partition,
  * then the last partition of every split sequence, so that its merge is done

@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     STATIC_SCRATCH_BYTES,
     append_paged_decode_shared_prefix,
     copy_blocks,
+    decode_engine,
     decode_partition_size,
     decode_plan,
     decode_workspace_bytes,

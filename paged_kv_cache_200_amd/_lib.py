@@ -50,6 +50,7 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i64]),
+    "pkv_decode_engine": (_i32, [_i32, _i32, _i32, _i32]),
     "pkv_paged_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                         _i32, _vp]),

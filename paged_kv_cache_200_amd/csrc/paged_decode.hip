@@ -286,8 +286,11 @@ __device__ __forceinline__ bool resolve_unit(Unit& un, int order, int num_kv_hea
     // instead of dependent ones before the first block-table read.
     const int unit = blockIdx.x / num_kv_heads;
     un.kvh = blockIdx.x - unit * num_kv_heads;
-    if (unit >= *plan_count) return false;
+    // both loads at once: the grid never exceeds the plan's batch * np entries, so the
+    // entry is readable (stale) even past the count
+    const int count = *plan_count;
     const int4 u = plan[unit];
+    if (unit >= count) return false;
     un.s = u.x;
     un.tok0 = u.y;
     un.tok1 = u.z;
@@ -327,10 +330,14 @@ __device__ __forceinline__ bool resolve_unit(Unit& un, int order, int num_kv_hea
 // Epilogue of a split unit whose sequence is merged in this launch, after its partial
 // results were stored with device-scope stores: wait until those stores have completed,
 // take one ticket per workgroup from the (sequence, KV head) counter, and if it is the
-// last of the sequence's n_merge units, merge every slot (the log-sum-exp combine, same
-// routine and order as the combine kernel; wave w merges query heads w, w + NW, ...) and
-// reset the counter.  The counter is zeroed by the plan, so a reused plan starts from zero
-// too.  Called by all threads of the workgroup.
+// last of the sequence's n_merge units (n_merge <= kMaxInPassMergeSlots), merge every slot
+// (the log-sum-exp combine in the combine kernel's arithmetic and order; wave w merges
+// query heads w, w + NW, ...) and reset the counter.  The counter is zeroed by the plan,
+// so a reused plan starts from zero too.  Called by all threads of the workgroup.
+//
+// The merging wave issues every load of its heads (log-sum-exps and partial outputs of
+// all slots) before it waits for any: one round trip to memory instead of one for the
+// log-sum-exps and another for the outputs, per head.
 template <int D, int G, int NW>
 __device__ __forceinline__ void merge_when_last(int n_merge, int* __restrict__ merge_ctr, int s,
                                                 int kvh, int num_q_heads, int num_kv_heads,
@@ -347,11 +354,47 @@ __device__ __forceinline__ void merge_when_last(int n_merge, int* __restrict__ m
   if (leader) s_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_ticket == n_merge - 1) {
-    for (int g = wave; g < G; g += NW) {
+    constexpr int kRows = (G + NW - 1) / NW;  // heads per wave
+    constexpr int kSlots = kMaxInPassMergeSlots;
+    constexpr int kPer = D / kWave;           // output dims per lane
+    constexpr float kLog2e = 1.44269504088896340736f;
+    float lp[kRows];
+    float x[kRows][kSlots][kPer];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int g = wave + r * NW;
+      const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + min(g, G - 1);
+      const float* pl = part_lse + sh * max_parts;
+      const float* po = part_out + sh * max_parts * D;
+      lp[r] = g < G && lane < n_merge ? load_partial<true>(pl + lane) : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          x[r][u][j] = g < G && u < n_merge ? load_partial<true>(po + u * D + j * kWave + lane)
+                                            : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int g = wave + r * NW;
+      if (g >= G) continue;
       const size_t sh = static_cast<size_t>(s) * num_q_heads + kvh * G + g;
-      combine_row<D, true, kInPassMergeChunk>(out + sh * D, lse != nullptr ? lse + sh : nullptr,
-                              part_lse + sh * max_parts, part_out + sh * max_parts * D, n_merge,
-                              lane);
+      const float M = wave_max(lp[r]);
+      const float w = lp[r] == -INFINITY ? 0.0f : fast_exp2((lp[r] - M) * kLog2e);
+      const float den = wave_sum(w);
+      float acc[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kSlots; ++u) {
+        const float wp = __shfl(w, u);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp, x[r][u][j], acc[j]);
+      }
+      float* out_row = out + sh * D;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) out_row[j * kWave + lane] = den > 0.0f ? acc[j] / den : 0.0f;
+      if (lse != nullptr && lane == 0) lse[sh] = den > 0.0f ? M + __logf(den) : -INFINITY;
     }
     if (leader) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1474,6 +1517,18 @@ extern "C" int32_t pkv_decode_partition_size(int32_t batch, int32_t num_kv_heads
   while (merge_p < per_merge) merge_p *= 2;
   if (merge_p <= 2 * P) P = min(max(P, merge_p), 8192);
   return P >= max_context_len ? 0 : P;
+}
+
+extern "C" int32_t pkv_decode_engine(int32_t dtype, int32_t head_dim, int32_t num_q_heads,
+                                     int32_t num_kv_heads) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if ((head_dim != 64 && head_dim != 128) || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 8)
+    return PKV_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  const bool tile = dtype == PKV_BF16 &&
+                    (head_dim == 64 ? pkv::mfma_pass<uint16_t, 64>(G) : pkv::mfma_pass<uint16_t, 128>(G));
+  return tile ? PKV_ENGINE_MATRIX : PKV_ENGINE_VALU;
 }
 
 extern "C" size_t pkv_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads,

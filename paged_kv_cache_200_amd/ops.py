@@ -115,6 +115,19 @@ def decode_partition_size(batch, num_kv_heads, head_dim, max_context_len,
                                                     int(total_context_tokens)))
 
 
+def decode_engine(kv_dtype, head_dim, num_q_heads, num_kv_heads) -> str:
+    """Which first pass the decode calls run for these shapes (pkv_decode_engine):
+    "valu" (decode_pass1_kernel) or "matrix" (the bf16 matrix-core tile)."""
+    codes = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16}
+    if kv_dtype not in codes:
+        raise TypeError(f"unsupported K/V dtype {kv_dtype!r} ('f32' or 'bf16')")
+    code = int(_lib.lib().pkv_decode_engine(codes[kv_dtype], head_dim, num_q_heads,
+                                            num_kv_heads))
+    if code < 0:
+        _lib.check("pkv_decode_engine", code)
+    return "matrix" if code == 1 else "valu"
+
+
 def shared_prefix_workspace_bytes(batch, num_q_heads, head_dim, max_context_len,
                                   partition_size) -> int:
     return int(_lib.lib().pkv_shared_prefix_workspace_bytes(batch, num_q_heads, head_dim,

@@ -43,3 +43,17 @@ def test_rule_edges(rule):
             P = rule(B, 8, 128, n, B * n)
             assert P == 0 or (256 <= P <= 8192 and P & (P - 1) == 0 and P < n)
     assert rule(0, 8, 128, 4096, 0) == 0 and rule(4, 0, 128, 4096, 0) == 0
+
+
+def test_engine_choice():
+    """pkv_decode_engine: the bf16 matrix-core tile for groups of 7 and 8, the VALU pass
+    otherwise; shapes the decode calls refuse are refused here too."""
+    import paged_kv_cache_200_amd as pkv
+    for d in (64, 128):
+        for g in range(1, 9):
+            want = "matrix" if g >= 7 else "valu"
+            assert pkv.decode_engine("bf16", d, 2 * g, 2) == want, (d, g)
+            assert pkv.decode_engine("f32", d, 2 * g, 2) == "valu", (d, g)
+    for bad in (("bf16", 96, 8, 8), ("bf16", 128, 18, 2), ("bf16", 128, 9, 2)):
+        with pytest.raises(Exception):
+            pkv.decode_engine(*bad)
