@@ -454,8 +454,23 @@ __device__ __forceinline__ unsigned mfma_tile(
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const size_t sh = static_cast<size_t>(row0 + mi) * num_q_heads + kvh * G + row % G;
     float* dst = dst_out + (sh * slots + slot) * D + cc * Mg::kTiles;
+    if constexpr (kAgentStores) {
+      // Device-scope stores write through one 4-byte store per lane and instruction:
+      // thread cc takes dims cc, cc + 16, ... so that each instruction covers 16
+      // consecutive floats of the row (the same sums as below, element by element).
+      float* drow = dst_out + (sh * slots + slot) * D;
 #pragma unroll
-    for (int u = 0; u < kQuads; ++u) {
+      for (int k = 0; k < Mg::kTiles; ++k) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w)
+          acc = fmaf(e[w], reinterpret_cast<const float*>(&sm.o[w][row][0])[cc + 16 * k], acc);
+        __hip_atomic_store(drow + cc + 16 * k, acc * inv, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < (kAgentStores ? 0 : kQuads); ++u) {
       float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
       for (int w = 0; w < kTileWaves; ++w) {
@@ -467,14 +482,7 @@ __device__ __forceinline__ unsigned mfma_tile(
       }
       acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
       // dims cc * D/16 + j of tile j: float4 u holds tiles 4u .. 4u + 3
-      if constexpr (kAgentStores) {
-        __hip_atomic_store(dst + 4 * u + 0, acc.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 4 * u + 1, acc.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 4 * u + 2, acc.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 4 * u + 3, acc.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        *reinterpret_cast<float4*>(dst + 4 * u) = acc;
-      }
+      *reinterpret_cast<float4*>(dst + 4 * u) = acc;
     }
     if (cc == 0 && dst_lse != nullptr) {
       const float ls = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
