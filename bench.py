@@ -273,7 +273,7 @@ def run_prefill(args, np, torch, pkv):
         "query_tokens_per_s": round(T / step_s, 1),
         "flops_per_step": flops,
         "roofline": {
-            "kernel": "prefill_lds_kernel",
+            "kernel": "prefill_t32_kernel",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -6,10 +6,11 @@
 // included): query i sits at position n - q_len + i and attends to tokens [0, that
 // position], through the block table, with explicit lengths.
 //
-// bf16 caches: matrix-core row tiles of 16 (token, query head) rows of one sequence for
-// one KV head, each row with its own causal limit; a workgroup's four waves take
-// consecutive tiles and share every K/V block through LDS.  fp32 caches: the VALU
-// routine of the decode, one wave per query token.
+// bf16 caches: matrix-core tiles of 32 (token, query head) rows of one sequence for one
+// KV head on the 32x32x16 shape, each row with its own causal limit; a workgroup's four
+// waves take consecutive tiles and share every pair of K/V blocks through LDS, and all
+// workgroups of one (sequence, KV head) run on one XCD so its blocks are reused from one
+// L2.  fp32 caches: the VALU routine of the decode, one wave per query token.
 
 #include "common.h"
 
@@ -55,255 +56,136 @@ __device__ __forceinline__ Chunk chunk_of(const int32_t* __restrict__ cu_q,
   return c;
 }
 
-// bf16, LDS-staged: a workgroup of four waves takes kR row tiles per wave, i.e.
-// 4 * kR * (16 / G) consecutive query tokens of one sequence for one KV head.  Each block
-// of the causal range is loaded once per workgroup (every thread fetches 16 bytes of K
-// and of V, so the loads in flight cost few registers), stored to LDS with rows padded by
-// 32 bytes (both operand reads and the stores then touch distinct banks), and read by
-// every wave for all its row tiles: one block load serves 64 * kR rows.  Three LDS stages
-// and three register sets: a block's loads are issued two blocks before it is stored, the
-// next block is stored while the current one is read, one barrier per block.
+// bf16: four waves per workgroup (kLdsThreads threads), each wave 32 (token, query head)
+// rows of one sequence for one KV head, i.e. 4 * (32 / G) consecutive query tokens.  Each
+// pair of cache blocks in the group's causal range is loaded once per workgroup into LDS
+// and read by all four waves.
 constexpr int kLdsWaves = 4;
 constexpr int kLdsThreads = kLdsWaves * kWave;
 
-template <int D>
-struct LdsStage {
-  // K rows: 32-byte pad per token row.  With a 16-byte pad the K operand reads (16 bytes
-  // per lane, rows c = 0..15) conflicted on the banks: 37 M conflict cycles per call of
-  // the 16 x 512-token chunked prefill, 0 with this pad, and the call ran 2-3% faster.
-  static constexpr int kRowElems = D + 16;
-  static constexpr int kVRowElems = D + 16;  // V rows: 32-byte pad (the transpose reads below
-                                             // then touch each bank window once per pass)
-  alignas(16) uint16_t k[kBlockTokens * kRowElems];
-  alignas(16) uint16_t v[kBlockTokens * kVRowElems];
-};
-
-template <int D>
-struct StageRegs {
-  static constexpr int kChunks = 2 * kBlockTokens * D / 8;  // 16-byte chunks of K and V
-  static constexpr int kPerThread = (kChunks + kLdsThreads - 1) / kLdsThreads;
-  u32x4_t w[kPerThread];
-};
-
-// Chunk i of a block: i < 2D covers K (token i / (D/8), dims 8 * (i % (D/8)) ..), the rest V.
-template <int D>
-__device__ __forceinline__ void stage_load(StageRegs<D>& r, const uint16_t* __restrict__ kt,
-                                           const uint16_t* __restrict__ vt, int tid) {
-  constexpr int kHalf = StageRegs<D>::kChunks / 2;
-#pragma unroll
-  for (int j = 0; j < StageRegs<D>::kPerThread; ++j) {
-    const int i = tid + j * kLdsThreads;
-    const uint16_t* src = i < kHalf ? kt + i * 8 : vt + (i - kHalf) * 8;
-    r.w[j] = *reinterpret_cast<const u32x4_t*>(src);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void stage_store(LdsStage<D>& st, const StageRegs<D>& r, int tid) {
-  constexpr int kHalf = StageRegs<D>::kChunks / 2;
-  constexpr int kRowChunks = D / 8;
-#pragma unroll
-  for (int j = 0; j < StageRegs<D>::kPerThread; ++j) {
-    const int i = tid + j * kLdsThreads;
-    const int ii = i < kHalf ? i : i - kHalf;
-    uint16_t* dst = (i < kHalf ? st.k : st.v) +
-                    (ii / kRowChunks) * (i < kHalf ? LdsStage<D>::kRowElems
-                                                   : LdsStage<D>::kVRowElems) +
-                    (ii % kRowChunks) * 8;
-    *reinterpret_cast<u32x4_t*>(dst) = r.w[j];
-  }
-}
-
-// The lane's MFMA operands of a staged block.  K as in mfma_load_block.  V through the
-// gfx950 LDS transpose read: within each 16-lane group, ds_read_b64_tr_b16 gives lane i
-// element i % 4 of the 8-byte chunks addressed by lanes i / 4 + 4k (k = 0..3), so lane
-// (c, h) addressing V[4h + c / 4][16j + 4 (c % 4)] receives V[4h .. 4h + 3][16j + c]: the
-// B operand of output tile j (dims 16j .. 16j + 15, lane c holding dim 16j + c), with no
-// repacking on the VALU.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
-template <int D>
-struct TrBlock {
-  u32x4_t k[MfmaGeom<D>::kQkSteps];
-  u32x2_t vt[MfmaGeom<D>::kTiles];  // tile j: V[4h .. 4h + 3][16j + c], two tokens a word
-};
-
-template <int D>
-__device__ __forceinline__ void stage_read_tr(TrBlock<D>& b, const LdsStage<D>& st, int c,
-                                              int h) {
-  using Mg = MfmaGeom<D>;
-  constexpr int RS = LdsStage<D>::kRowElems;
-  constexpr int RV = LdsStage<D>::kVRowElems;
-#pragma unroll
-  for (int k = 0; k < Mg::kQkSteps; ++k)
-    b.k[k] = *reinterpret_cast<const u32x4_t*>(st.k + c * RS + 32 * k + 8 * h);
-  const uint16_t* vrow = st.v + (4 * h + c / 4) * RV + 4 * (c % 4);
-#pragma unroll
-  for (int j = 0; j < Mg::kTiles; ++j) {
-    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16_t*)(vrow + 16 * j));
-    b.vt[j] = __builtin_bit_cast(u32x2_t, t);
-  }
-}
-
-// One block for a wave's 16 rows on a transpose-read block: scores as in mfma_rows_block,
-// then P rounded once to bf16 (round to nearest even, two values per v_cvt_pk_bf16_f32) as
-// the A operand of a 16x16x16 product per output tile, whose B operand is the transposed
-// V pair as read (output tile j holds dims 16j + c).  kMasked: some row's causal limit or
-// the chunk's end falls inside the block, so scores are masked per row; blocks below every
-// row's limit skip the compares.
-typedef short v4i16_t2 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
 
+// ---- 32-row tiles on the 32x32x16 matrix-core shape ----
+//
+// A wave owns 32 (token, query head) rows; each step takes 32 keys (two cache blocks).
+// Scores are computed transposed, S^T = K Q^T: lane l holds row l % 32's scores for keys
+// 8i + 4(l / 32) + j (i, j < 4), so every softmax statistic of a row lives on lanes l and
+// l ^ 32.  The output is held transposed too, O^T = V^T P^T, so a lane's accumulators all
+// belong to its row and a rescale is one multiply per accumulator.  The contraction runs
+// over the keys in the order the score tile holds them: per 16-key step, lanes below 32
+// take keys {0..3, 8..11}, the others {4..7, 12..15}; the V^T operand follows that order
+// through two LDS transpose reads per product.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kT32Rows = 32;
+constexpr int kPairTokens = 2 * kBlockTokens;
+constexpr int kXcds = 8;  // MI355X: eight accelerator complex dies
+
+// LDS image of a staged pair: K rows then V rows, 32 tokens each.  K rows are padded by
+// 16 bytes and V rows by 32; V row t sits at position vpos(t), the order 0, 4, 1, 5, 2, 6,
+// 3, 7 within each 8 tokens, so the four consecutive rows one transpose read meets sit two
+// positions apart.  With these pads neither the K operand reads nor the V transpose reads
+// meet a bank conflict (shader counters on the 16 x 512-token chunked prefill: 0 conflict
+// cycles, against 18.7 M with 32-byte K pads and 37 M with 32-byte pads and V in order).
 template <int D>
-__device__ __forceinline__ void tr_rows_block(MfmaRows<D>& r, TrBlock<D>& cur,
-                                              const u32x4_t (&qr)[MfmaGeom<D>::kQkSteps],
-                                              int t_base, int n_c, int n_max, int h,
-                                              float scale_log2, bool masked) {
-  using Mg = MfmaGeom<D>;
-  f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int s = 0; s < Mg::kQkSteps; ++s)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
-                                                 __builtin_bit_cast(bf16x8_t, qr[s]), sc, 0, 0,
-                                                 0);
-  float x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = sc[i] * scale_log2;
-  if (masked) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (t_base + 4 * h + i < n_c) ? x[i] : -INFINITY;
-  }
-  float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  bm = max_xor32(max_xor16(bm));
-  const bool raise = bm > r.m_c + kLazyMaxSlack;
-  if (__any(raise)) {
-    float a = 1.0f;
-    if (raise) {
-      a = r.m_c == -INFINITY ? 0.0f : fast_exp2(r.m_c - bm);
-      r.m_c = bm;
-    }
-    r.l_part *= a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(a, 4 * h + i);
-#pragma unroll
-      for (int j = 0; j < Mg::kTiles; ++j) r.o[j][i] *= ai;
-    }
-  }
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // No select for masked scores: exp2(-inf - m) is 0 once m is finite, and every live
-    // row's m is finite from block 0 on (block 0 comes first and holds token 0, which every
-    // causal row attends).  Rows past the chunk's last token keep m = -inf and turn NaN;
-    // matrix-core rows are independent and those rows are never written.
-    p[i] = fast_exp2(x[i] - r.m_c);
-    r.l_part += p[i];
-  }
-  bf16x2_t2 p01, p23;
-  p01[0] = static_cast<__bf16>(p[0]);
-  p01[1] = static_cast<__bf16>(p[1]);
-  p23[0] = static_cast<__bf16>(p[2]);
-  p23[1] = static_cast<__bf16>(p[3]);
-  const v4i16_t2 a = __builtin_bit_cast(
-      v4i16_t2, u32x2_t{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)});
-  // Tokens past every taken row's end hold stale data: zero their V (0 * NaN); word 0 holds
-  // tokens 4h, 4h + 1 (low, high half), word 1 tokens 4h + 2, 4h + 3.
-  if (t_base + kBlockTokens > n_max) {
-    const int t0 = t_base + 4 * h;
-    const uint32_t m0 = (t0 < n_max ? 0x0000ffffu : 0u) | (t0 + 1 < n_max ? 0xffff0000u : 0u);
-    const uint32_t m1 = (t0 + 2 < n_max ? 0x0000ffffu : 0u) | (t0 + 3 < n_max ? 0xffff0000u : 0u);
-#pragma unroll
-    for (int j = 0; j < Mg::kTiles; ++j) {
-      cur.vt[j][0] &= m0;
-      cur.vt[j][1] &= m1;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < Mg::kTiles; ++j)
-    r.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(v4i16_t2, cur.vt[j]),
-                                                       r.o[j], 0, 0, 0);
+struct PairLayout {
+  static constexpr int kRowElems = D + 8;
+  static constexpr int kVRowElems = D + 16;
+  static constexpr int kVBase = kPairTokens * kRowElems;                // elements
+  static constexpr int kStage = kPairTokens * (kRowElems + kVRowElems);  // per stage
+  static constexpr int kPartChunks = kBlockTokens * D / 8;     // one block's K (or V) slice
+  static constexpr int kPerThread = 4 * kPartChunks / kLdsThreads;
+  static_assert(4 * kPartChunks % kLdsThreads == 0 && kLdsThreads % kPartChunks == 0,
+                "a thread's chunks sit at one offset of every part they touch");
+};
+__device__ __forceinline__ int vpos(int row) {
+  return (row & ~7) | ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
-// Row tiles per wave of the bf16 prefill (each LDS read of a block serves kR tiles), and
-// workgroups per compute unit the register allocation is held to.
-#ifndef PKV_PREFILL_ROW_TILES
-#define PKV_PREFILL_ROW_TILES 1
-#endif
-constexpr int kPrefillRowTiles = PKV_PREFILL_ROW_TILES;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
 
-template <int D, int G, int kR>
-__global__ __launch_bounds__(kLdsThreads, kR == 1 ? 4 : 2) void prefill_lds_kernel(
+template <int D, int G>
+__global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables, int W,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens, int total_q,
     int max_q_len, int num_q_heads, int num_kv_heads, int num_blocks, float scale_log2,
-    float* __restrict__ out, float* __restrict__ lse) {
-  using Mg = MfmaGeom<D>;
-  constexpr int kMembers = kMfmaRows / G;  // query tokens per row tile
+    float* __restrict__ out, float* __restrict__ lse, int batch) {
+  using Ly = PairLayout<D>;
+  constexpr int kSteps = D / 16;          // 32x32x16 products per score tile
+  constexpr int kDimTiles = D / 32;       // output tiles of 32 dims
+  constexpr int kMembers = kT32Rows / G;  // query tokens per wave
   constexpr int kRows = kMembers * G;
-  constexpr int kGroupTokens = kMembers * kR * kLdsWaves;
-  __shared__ LdsStage<D> stage[3];
+  constexpr int kGroupTokens = kMembers * kLdsWaves;
+  constexpr int RS = Ly::kRowElems;
+  constexpr int kRowChunks = D / 8;
+  __shared__ alignas(16) uint16_t smem[2 * Ly::kStage];
   __shared__ int s_ids[kLdsThreads];
-  const int s = blockIdx.y;
-  const int kvh = blockIdx.z;
+  // Workgroups go to the eight XCDs round-robin in launch order (workgroup L to XCD
+  // L % 8), each XCD with its own L2.  All row groups of one (sequence, KV head) unit are
+  // placed on one XCD, so the unit's K/V blocks are fetched into one L2 and reused there:
+  // unit u = 8j + x runs on XCD x as its j-th unit, groups consecutively.
+  const int n_groups = (max_q_len + kGroupTokens - 1) / kGroupTokens;
+  const int wg = blockIdx.x;
+  const int xk = wg / kXcds;
+  const int unit = (xk / n_groups) * kXcds + wg % kXcds;
+  const int gx = xk % n_groups;
+  if (unit >= batch * num_kv_heads) return;  // padding of the last round: uniform
+  const int s = unit / num_kv_heads;
+  const int kvh = unit % num_kv_heads;
   const int tid = threadIdx.x;
-  const bool first = blockIdx.x == 0 && kvh == 0 && tid == 0;
+  const bool first = gx == 0 && kvh == 0 && tid == 0;
   const Chunk ch = chunk_of(cu_q, ctx_lens, s, total_q, max_q_len, W * kBlockTokens, first);
   const int groups = (ch.len + kGroupTokens - 1) / kGroupTokens;
-  if (static_cast<int>(blockIdx.x) >= groups) return;  // whole workgroup: uniform
+  if (gx >= groups) return;  // whole workgroup: uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int c = lane % 16;
-  const int h = lane / 16;
-  const int tg = (groups - 1 - static_cast<int>(blockIdx.x)) * kGroupTokens;  // group's first
+  const int r = lane % 32;  // the lane's row
+  const int h = lane / 32;  // which half of each 8-key run the lane holds
+  const int tg = (groups - 1 - gx) * kGroupTokens;
   const int pos_g = ch.n - ch.len + tg;
-  // The group's causal range ends at its last live token.
   const int g_members = min(kGroupTokens, ch.len - tg);
   const int n_group = pos_g + g_members;
   const int nblk = (n_group + kBlockTokens - 1) / kBlockTokens;
 
-  // This wave's row tiles: tokens tg + (wave * kR + r) * kMembers + c / G.
-  int n_c[kR], members[kR], tile_end[kR];
-  int tile_lim0[kR];  // the smallest causal limit of the tile's rows (its first token's)
-  int n_wave = 0;
-  u32x4_t qr[kR][Mg::kQkSteps];
-  MfmaRows<D> rows[kR];
+  // This wave's rows: tokens t0 + r / G, heads r % G.
+  const int t0 = tg + wave * kMembers;
+  const int members = max(0, min(kMembers, ch.len - t0));
+  const int pos0 = ch.n - ch.len + t0;
+  const bool live = r < kRows && r / G < members;
+  const int n_c = live ? pos0 + r / G + 1 : 0;
+  const int n_wave = members > 0 ? pos0 + members : 0;
+  const int lim0 = pos0 + 1;  // the smallest causal limit of the wave's rows
+  u32x4_t qr[kSteps];
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int t0 = tg + (wave * kR + r) * kMembers;
-    members[r] = max(0, min(kMembers, ch.len - t0));
-    const int pos0 = ch.n - ch.len + t0;
-    const bool live = c < kRows && c / G < members[r];
-    n_c[r] = live ? pos0 + c / G + 1 : 0;
-    tile_end[r] = members[r] > 0 ? pos0 + members[r] : 0;
-    tile_lim0[r] = pos0 + 1;
-    n_wave = max(n_wave, tile_end[r]);
+  for (int k = 0; k < kSteps; ++k) qr[k] = u32x4_t{0u, 0u, 0u, 0u};
+  if (live) {
+    const uint16_t* qrow =
+        q + (static_cast<size_t>(ch.r0 + t0 + r / G) * num_q_heads + kvh * G + r % G) * D + 8 * h;
 #pragma unroll
-    for (int k = 0; k < Mg::kQkSteps; ++k) qr[r][k] = u32x4_t{0u, 0u, 0u, 0u};
-    if (live) {
-      const uint16_t* qrow = q + (static_cast<size_t>(ch.r0 + t0 + c / G) * num_q_heads +
-                                  kvh * G + c % G) * D + 8 * h;
-#pragma unroll
-      for (int k = 0; k < Mg::kQkSteps; ++k)
-        qr[r][k] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * k);
-    }
-    mfma_rows_init<D>(rows[r]);
+    for (int k = 0; k < kSteps; ++k)
+      qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * k);
   }
+  f32x16_t o[kDimTiles];
+#pragma unroll
+  for (int dt = 0; dt < kDimTiles; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  const bf16x2_t2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   // The query loads above are conditional; without this wait the compiler cannot prove
-  // them complete at the block loop's head and waits for every outstanding load (the
-  // staged blocks' too) before each block's first matrix product.
+  // them complete at the loop's head and waits for every load in flight (the staged
+  // pairs' too) before each pair's first product.
   __builtin_amdgcn_s_waitcnt(0);
 
   const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
   const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
   const int32_t* trow = tables + static_cast<size_t>(s) * W;
-  // Block ids, a window of kLdsThreads at a time (one per thread), in LDS.  Each window
-  // is streamed on its own, so the block loop itself holds no table read.
-  auto block_ptr = [&](int id, const uint16_t* base) {
-    return base + static_cast<size_t>(id) * block_elems + kvh * head_elems;
-  };
   auto fetch_ids = [&](int from) {
     const int k = from + tid;
     const int id = k < nblk ? trow[k] : 0;
@@ -311,80 +193,187 @@ __global__ __launch_bounds__(kLdsThreads, kR == 1 ? 4 : 2) void prefill_lds_kern
     if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
     s_ids[tid] = bad ? 0 : id;
   };
-  auto compute = [&](const LdsStage<D>& st, int b) {
-    const int t_base = b * kBlockTokens;
-    if (t_base >= n_wave) return;  // past every row of this wave (causal): nothing to add
-    TrBlock<D> cur;
-    stage_read_tr<D>(cur, st, c, h);
+
+  // Staging: a pair is four parts of 16-byte chunks (K of block 0, K of block 1, V of
+  // block 0, V of block 1; 16 rows x D/8 chunks each).  Chunk j * 256 + tid goes through
+  // thread tid, so a wave's chunks lie in one part (uniform base address) and the
+  // thread's offset into every part is the same: chunk c of row c_row.
+  const int c = tid % Ly::kPartChunks;
+  const int c_row = c / kRowChunks;
+  const uint32_t g_off = 16u * c;                    // bytes into the part
+  const uint32_t g_off0 = 16u * (c % kRowChunks);    // the same column of the block's row 0
+  const int s_k = c_row * RS + 8 * (c % kRowChunks);          // LDS element offsets
+  constexpr int RV = Ly::kVRowElems;
+  const int s_v = Ly::kVBase + vpos(c_row) * RV + 8 * (c % kRowChunks);
+  u32x4_t rr[Ly::kPerThread];
+  // V rows at or past `lim` (pair-relative: past the context's end, stale slots) are
+  // fetched from the block's first row instead, which holds a real token, so their zero
+  // weights meet finite values.
+  auto pair_load = [&](int id0, int id1, int lim) {
+    const char* k0 = reinterpret_cast<const char*>(kc + id0 * block_elems + kvh * head_elems);
+    const char* k1 = reinterpret_cast<const char*>(kc + id1 * block_elems + kvh * head_elems);
+    const char* v0 = reinterpret_cast<const char*>(vc + id0 * block_elems + kvh * head_elems);
+    const char* v1 = reinterpret_cast<const char*>(vc + id1 * block_elems + kvh * head_elems);
 #pragma unroll
-    for (int r = 0; r < kR; ++r)
-      if (t_base < tile_end[r])
-        tr_rows_block<D>(rows[r], cur, qr[r], t_base, n_c[r], n_wave, h, scale_log2,
-                         t_base + kBlockTokens > tile_lim0[r]);
+    for (int j = 0; j < Ly::kPerThread; ++j) {
+      const int part = (j * kLdsThreads + wave * kWave) / Ly::kPartChunks;  // uniform
+      const char* base = part == 0 ? k0 : part == 1 ? k1 : part == 2 ? v0 : v1;
+      const uint32_t off =
+          part >= 2 && (part - 2) * kBlockTokens + c_row >= lim ? g_off0 : g_off;
+      rr[j] = *reinterpret_cast<const u32x4_t*>(base + off);
+    }
+  };
+  auto pair_store = [&](int stage) {
+#pragma unroll
+    for (int j = 0; j < Ly::kPerThread; ++j) {
+      const int part = (j * kLdsThreads + wave * kWave) / Ly::kPartChunks;  // uniform
+      const int at = stage * Ly::kStage + (part < 2 ? s_k + (part % 2) * kBlockTokens * RS
+                                                    : s_v + (part % 2) * kBlockTokens * RV);
+      *reinterpret_cast<u32x4_t*>(smem + at) = rr[j];
+    }
   };
 
-  // Three LDS stages, three register sets: the loads of block j are issued two blocks
-  // before it is stored to LDS (block j lives in stage (j - w0) % 3).  Past the window's
-  // last block that block is loaded and stored again (a cache hit, never read): every
-  // load and store of the loop is then unconditional, so the compiler's wait before a
-  // stage store counts only the loads that filled it, not the ones issued after.
-  StageRegs<D> r0, r1, r2;
+  // K operand: row r, dims 16k + 8h ..; V^T operand reads: lane (g = lane / 16,
+  // q = lane % 16) addresses V[16t + 4h + q / 4 (+ 8)][32 dt + 16 (g % 2) + 4 (q % 4)] and
+  // receives four keys of dim 32 dt + r.
+  const int k_at = r * RS + 8 * h;
+  const int vq = lane % 16;
+  const int v_at = Ly::kVBase + vpos(4 * h + vq / 4) * RV + 16 * ((lane / 16) % 2) + 4 * (vq % 4);
+  auto scores = [&](int stage, f32x16_t& sc) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) {
+      const u32x4_t a =
+          *reinterpret_cast<const u32x4_t*>(smem + k_at + stage * Ly::kStage + 16 * k);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, qr[k]), sc, 0,
+                                                   0, 0);
+    }
+  };
+  auto attend = [&](int stage, const f32x16_t& sc, int t_base) {
+    // Scores in log2 units, masked ones -inf (a select, so stale keys' NaN scores drop
+    // out).  The scale is applied before the max, so the max key's weight is exactly 1.
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = sc[e] * scale_log2;
+    if (t_base + kPairTokens > lim0) {
+      const int lim = n_c - t_base - 4 * h;  // keys 8i + j of the lane below lim are attended
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[4 * i + j] = (8 * i + j < lim) ? x[4 * i + j] : -INFINITY;
+    }
+    float bm = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) bm = fmaxf(bm, x[e]);
+    bm = max_xor32(bm);
+    const bool raise = bm > m + kLazyMaxSlack;
+    if (__any(raise)) {
+      float a = 1.0f;
+      if (raise) {
+        a = m == -INFINITY ? 0.0f : fast_exp2(m - bm);
+        m = bm;
+      }
+      l *= a;
+#pragma unroll
+      for (int dt = 0; dt < kDimTiles; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= a;
+    }
+    // No select for masked weights: exp2(-inf - m) is 0 once m is finite, and every live
+    // row's m is finite from pair 0 on (it holds token 0, which every causal row attends).
+    // Rows past the chunk's last token keep m = -inf and turn NaN; the products keep rows
+    // (columns of the transposed tiles) apart, and those rows are never written.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[8 * t + e] - m);
+      // (The packed words are kept as four scalars: read back as elements of the operand
+      // vector, the ROCm 7.2 compiler fed the first word to all four dot products.)
+      uint32_t pw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pw[w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+      // The row sum takes the weights as the products do, rounded to bf16: the output is
+      // an exact convex combination of V rows under the rounded weights (a key whose
+      // weight rounds to 1 alone returns its V row exactly).
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t2, pw[w]), kOnes2, l,
+                                            false);
+      const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+      for (int dt = 0; dt < kDimTiles; ++dt) {
+        const uint16_t* vp = smem + v_at + stage * Ly::kStage + 16 * t * RV + 32 * dt;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vp));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vp + 8 * RV));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+        const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        __builtin_bit_cast(bf16x8_t, pb), o[dt],
+                                                        0, 0, 0);
+      }
+    }
+  };
+
+  // Two LDS stages and one register set: pair p + 1's loads are issued after pair p - 1's
+  // products and stored to the free stage once pair p's scores are read, so the staging
+  // registers are not live while pair p's products hold theirs.  One barrier per pair.
+  // Past the window's last block the last block is loaded again (never read), so every
+  // load and store of the loop is unconditional.
   for (int w0 = 0; w0 < nblk; w0 += kLdsThreads) {
     const int w1 = min(nblk, w0 + kLdsThreads);
     __syncthreads();  // the previous window's ids and stages are no longer read
     fetch_ids(w0);
     __syncthreads();
-    auto issue = [&](int j, StageRegs<D>& r) {
-      // uniform: the block's base address is computed on the scalar unit
-      const int id = __builtin_amdgcn_readfirstlane(s_ids[min(j, w1 - 1) - w0]);
-      stage_load<D>(r, block_ptr(id, kc), block_ptr(id, vc), tid);
+    auto issue = [&](int b) {
+      const int id0 = __builtin_amdgcn_readfirstlane(s_ids[min(b, w1 - 1) - w0]);
+      const int id1 = __builtin_amdgcn_readfirstlane(s_ids[min(b + 1, w1 - 1) - w0]);
+      pair_load(id0, id1, ch.n - b * kBlockTokens);
     };
-    issue(w0, r0);
-    issue(w0 + 1, r1);
-    issue(w0 + 2, r2);
-    stage_store<D>(stage[0], r0, tid);
+    issue(w0);
+    pair_store(0);
+    issue(w0 + 2);
     __syncthreads();
-    for (int b = w0; b < w1; b += 3) {
-      // stage[0] holds block b; r1, r2 hold blocks b + 1, b + 2 in flight
-      issue(b + 3, r0);
-      compute(stage[0], b);
-      stage_store<D>(stage[1], r1, tid);
+    auto step = [&](int cur, int b) {
+      const int t_base = b * kBlockTokens;
+      f32x16_t sc;
+      const bool act = t_base < n_wave;  // causal: past every row of this wave, nothing to add
+      if (act) scores(cur, sc);
+      pair_store(cur ^ 1);
+      if (act) attend(cur, sc, t_base);
+      issue(b + 4);
       __syncthreads();
-      if (b + 1 >= w1) break;
-      issue(b + 4, r1);
-      compute(stage[1], b + 1);
-      stage_store<D>(stage[2], r2, tid);
-      __syncthreads();
-      if (b + 2 >= w1) break;
-      issue(b + 5, r2);
-      compute(stage[2], b + 2);
-      stage_store<D>(stage[0], r0, tid);
-      __syncthreads();
+    };
+    for (int b = w0;;) {
+      step(0, b);
+      if ((b += 2) >= w1) break;
+      step(1, b);
+      if ((b += 2) >= w1) break;
     }
   }
 
-  // Row c's totals live on the four lanes with lane % 16 == c; output row 4h + i's on
-  // lane (c, h), dims 16j + c.  Each output row takes its max and sum from a lane owning its score row.
+  const float L = sum_xor32(l);
+  if (live) {
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const size_t sh = static_cast<size_t>(ch.r0 + t0 + r / G) * num_q_heads + kvh * G + r % G;
+    float* dst = out + sh * D + 4 * h;
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    float l_c = rows[r].l_part;
-        l_c = sum_xor32(sum_xor16(l_c));
-    const int t0 = tg + (wave * kR + r) * kMembers;
+    for (int dt = 0; dt < kDimTiles; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * h + i;
-      const float L = __shfl(l_c, rr);
-      const float M = __shfl(rows[r].m_c, rr);
-      if (rr >= kRows || rr / G >= members[r]) continue;
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      const size_t sh =
-          static_cast<size_t>(ch.r0 + t0 + rr / G) * num_q_heads + kvh * G + rr % G;
-      // output tile j holds dims 16j + c: each store writes 16 consecutive floats of a row
-      float* dst = out + sh * D + c;
-#pragma unroll
-      for (int j = 0; j < Mg::kTiles; ++j) dst[16 * j] = rows[r].o[j][i] * inv;
-      if (c == 0 && lse != nullptr) lse[sh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    }
+      for (int i = 0; i < 4; ++i) {
+        float4 v;
+        v.x = o[dt][4 * i + 0] * inv;
+        v.y = o[dt][4 * i + 1] * inv;
+        v.z = o[dt][4 * i + 2] * inv;
+        v.w = o[dt][4 * i + 3] * inv;
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * i) = v;
+      }
+    if (h == 0 && lse != nullptr) lse[sh] = L > 0.0f ? (m + __log2f(L)) * kLn2 : -INFINITY;
   }
 }
 
@@ -453,13 +442,16 @@ struct PrefillArgs {
 template <typename T, int D, int G>
 void prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    constexpr int kR = kPrefillRowTiles;
-    constexpr int kGroupTokens = kMfmaRows / G * kR * kLdsWaves;
-    const dim3 grid((a.max_q_len + kGroupTokens - 1) / kGroupTokens, a.batch, a.hkv);
-    hipLaunchKernelGGL((prefill_lds_kernel<D, G, kR>), grid, dim3(kLdsThreads), 0, stream,
+    // one workgroup per (row group, unit), grouped per XCD as the kernel decodes it
+    constexpr int kGroupTokens = kT32Rows / G * kLdsWaves;
+    const int n_groups = (a.max_q_len + kGroupTokens - 1) / kGroupTokens;
+    const int units = a.batch * a.hkv;
+    const dim3 grid(kXcds * ((units + kXcds - 1) / kXcds) * n_groups);
+    hipLaunchKernelGGL((prefill_t32_kernel<D, G>), grid, dim3(kLdsThreads), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.tables, a.W, a.cu_q, a.ctx,
-                       a.total_q, a.max_q_len, a.hq, a.hkv, a.nb, a.scale_log2, a.out, a.lse);
+                       a.total_q, a.max_q_len, a.hq, a.hkv, a.nb, a.scale_log2, a.out, a.lse,
+                       a.batch);
   } else {
     const dim3 grid((a.max_q_len + kPrefillWaves - 1) / kPrefillWaves, a.batch, a.hkv);
     hipLaunchKernelGGL((prefill_valu_kernel<T, D, G>), grid, dim3(kPrefillWaves * kWave), 0,
