@@ -125,7 +125,6 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
   constexpr int RS = Ly::kRowElems;
   constexpr int kRowChunks = D / 8;
   __shared__ alignas(16) uint16_t smem[2 * Ly::kStage];
-  __shared__ int s_ids[kLdsThreads];
   // Workgroups go to the eight XCDs round-robin in launch order (workgroup L to XCD
   // L % 8), each XCD with its own L2.  All row groups of one (sequence, KV head) unit are
   // placed on one XCD, so the unit's K/V blocks are fetched into one L2 and reused there:
@@ -186,12 +185,14 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
   const size_t head_elems = static_cast<size_t>(kBlockTokens) * D;
   const size_t block_elems = static_cast<size_t>(num_kv_heads) * head_elems;
   const int32_t* trow = tables + static_cast<size_t>(s) * W;
-  auto fetch_ids = [&](int from) {
-    const int k = from + tid;
-    const int id = k < nblk ? trow[k] : 0;
-    const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(num_blocks);
-    if (__any(bad) && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
-    s_ids[tid] = bad ? 0 : id;
+  // Block b's id, read one pair ahead of its use (b clamped to the range: past the end
+  // the last block is loaded again and never read); uniform, so a scalar load.  At use a
+  // bad id is flagged and read as block 0.
+  auto raw_id = [&](int b) { return trow[min(b, nblk - 1)]; };
+  auto checked = [&](int raw) {
+    const bool bad = static_cast<unsigned>(raw) >= static_cast<unsigned>(num_blocks);
+    if (bad && lane == 0) PKV_FLAG_ERROR(PKV_DEVERR_BLOCK_ID);
+    return __builtin_amdgcn_readfirstlane(bad ? 0 : raw);
   };
 
   // Staging: a pair is four parts of 16-byte chunks (K of block 0, K of block 1, V of
@@ -206,18 +207,24 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
   constexpr int RV = Ly::kVRowElems;
   const int s_v = Ly::kVBase + vpos(c_row) * RV + 8 * (c % kRowChunks);
   u32x4_t rr[Ly::kPerThread];
+  // Part of chunk j * 256 + tid (0: K of block 0, 1: K of block 1, 2: V of block 0, 3: V
+  // of block 1), written so that the compiler sees it is uniform.
+  auto part_of = [&](int j) {
+    return Ly::kPartChunks >= kLdsThreads ? j * (kLdsThreads / Ly::kPartChunks)
+                                          : j * (kLdsThreads / Ly::kPartChunks) +
+                                                wave / (Ly::kPartChunks / kWave);
+  };
   // V rows at or past `lim` (pair-relative: past the context's end, stale slots) are
   // fetched from the block's first row instead, which holds a real token, so their zero
   // weights meet finite values.
   auto pair_load = [&](int id0, int id1, int lim) {
-    const char* k0 = reinterpret_cast<const char*>(kc + id0 * block_elems + kvh * head_elems);
-    const char* k1 = reinterpret_cast<const char*>(kc + id1 * block_elems + kvh * head_elems);
-    const char* v0 = reinterpret_cast<const char*>(vc + id0 * block_elems + kvh * head_elems);
-    const char* v1 = reinterpret_cast<const char*>(vc + id1 * block_elems + kvh * head_elems);
+    const size_t o0 = static_cast<size_t>(id0) * block_elems + kvh * head_elems;
+    const size_t o1 = static_cast<size_t>(id1) * block_elems + kvh * head_elems;
 #pragma unroll
     for (int j = 0; j < Ly::kPerThread; ++j) {
-      const int part = (j * kLdsThreads + wave * kWave) / Ly::kPartChunks;  // uniform
-      const char* base = part == 0 ? k0 : part == 1 ? k1 : part == 2 ? v0 : v1;
+      const int part = part_of(j);  // uniform
+      const char* base =
+          reinterpret_cast<const char*>((part < 2 ? kc : vc) + (part % 2 ? o1 : o0));
       const uint32_t off =
           part >= 2 && (part - 2) * kBlockTokens + c_row >= lim ? g_off0 : g_off;
       rr[j] = *reinterpret_cast<const u32x4_t*>(base + off);
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
   auto pair_store = [&](int stage) {
 #pragma unroll
     for (int j = 0; j < Ly::kPerThread; ++j) {
-      const int part = (j * kLdsThreads + wave * kWave) / Ly::kPartChunks;  // uniform
+      const int part = part_of(j);  // uniform
       const int at = stage * Ly::kStage + (part < 2 ? s_k + (part % 2) * kBlockTokens * RS
                                                     : s_v + (part % 2) * kBlockTokens * RV);
       *reinterpret_cast<u32x4_t*>(smem + at) = rr[j];
@@ -323,38 +330,34 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
   // Two LDS stages and one register set: pair p + 1's loads are issued after pair p - 1's
   // products and stored to the free stage once pair p's scores are read, so the staging
   // registers are not live while pair p's products hold theirs.  One barrier per pair.
-  // Past the window's last block the last block is loaded again (never read), so every
-  // load and store of the loop is unconditional.
-  for (int w0 = 0; w0 < nblk; w0 += kLdsThreads) {
-    const int w1 = min(nblk, w0 + kLdsThreads);
-    __syncthreads();  // the previous window's ids and stages are no longer read
-    fetch_ids(w0);
+  // Block ids are read one pair ahead of their loads.  Past the last block the last block
+  // is loaded again (never read), so every load and store of the loop is unconditional.
+  int id_a = raw_id(0), id_b = raw_id(1);
+  pair_load(checked(id_a), checked(id_b), ch.n);
+  pair_store(0);
+  id_a = raw_id(2);
+  id_b = raw_id(3);
+  pair_load(checked(id_a), checked(id_b), ch.n - 2 * kBlockTokens);
+  id_a = raw_id(4);
+  id_b = raw_id(5);
+  __syncthreads();
+  auto step = [&](int cur, int b) {
+    const int t_base = b * kBlockTokens;
+    f32x16_t sc;
+    const bool act = t_base < n_wave;  // causal: past every row of this wave, nothing to add
+    if (act) scores(cur, sc);
+    pair_store(cur ^ 1);
+    if (act) attend(cur, sc, t_base);
+    pair_load(checked(id_a), checked(id_b), ch.n - (b + 4) * kBlockTokens);
+    id_a = raw_id(b + 6);
+    id_b = raw_id(b + 7);
     __syncthreads();
-    auto issue = [&](int b) {
-      const int id0 = __builtin_amdgcn_readfirstlane(s_ids[min(b, w1 - 1) - w0]);
-      const int id1 = __builtin_amdgcn_readfirstlane(s_ids[min(b + 1, w1 - 1) - w0]);
-      pair_load(id0, id1, ch.n - b * kBlockTokens);
-    };
-    issue(w0);
-    pair_store(0);
-    issue(w0 + 2);
-    __syncthreads();
-    auto step = [&](int cur, int b) {
-      const int t_base = b * kBlockTokens;
-      f32x16_t sc;
-      const bool act = t_base < n_wave;  // causal: past every row of this wave, nothing to add
-      if (act) scores(cur, sc);
-      pair_store(cur ^ 1);
-      if (act) attend(cur, sc, t_base);
-      issue(b + 4);
-      __syncthreads();
-    };
-    for (int b = w0;;) {
-      step(0, b);
-      if ((b += 2) >= w1) break;
-      step(1, b);
-      if ((b += 2) >= w1) break;
-    }
+  };
+  for (int b = 0;;) {
+    step(0, b);
+    if ((b += 2) >= nblk) break;
+    step(1, b);
+    if ((b += 2) >= nblk) break;
   }
 
   const float L = sum_xor32(l);
