@@ -109,6 +109,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// The sequence of rank r when sequences are ordered by causal work, largest first (ties
+// by index): a chunk of L tokens ending at context length n costs about L (2n - L + 1)
+// key-query pairs.  Each workgroup ranks the (few) sequences itself in LDS; the ranks
+// only order the launch, so a malformed length just misorders it.  Past kSortedBatch
+// sequences the launch keeps sequence order.  Called by all threads of the workgroup.
+constexpr int kSortedBatch = kLdsThreads;
+
+__device__ __forceinline__ int sequence_by_work(int r, const int32_t* __restrict__ cu_q,
+                                                const int32_t* __restrict__ ctx_lens, int batch,
+                                                int total_q, int tid) {
+  if (batch > kSortedBatch) return r;
+  __shared__ long long s_work[kSortedBatch];
+  __shared__ int s_seq;
+  long long w = -1;
+  if (tid < batch) {
+    const long long len = max(0, min(cu_q[tid + 1], total_q) - max(cu_q[tid], 0));
+    const long long n = max(ctx_lens[tid], 0);
+    w = len * (2 * n - len + 1);
+    s_work[tid] = w;
+  }
+  __syncthreads();
+  if (tid < batch) {
+    int rank = 0;
+    for (int t = 0; t < batch; ++t) {
+      const long long wt = s_work[t];
+      rank += (wt > w || (wt == w && t < tid)) ? 1 : 0;
+    }
+    if (rank == r) s_seq = tid;
+  }
+  __syncthreads();
+  return s_seq;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -128,16 +161,19 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
   // Workgroups go to the eight XCDs round-robin in launch order (workgroup L to XCD
   // L % 8), each XCD with its own L2.  All row groups of one (sequence, KV head) unit are
   // placed on one XCD, so the unit's K/V blocks are fetched into one L2 and reused there:
-  // unit u = 8j + x runs on XCD x as its j-th unit, groups consecutively.
+  // unit u = 8j + x runs on XCD x as its j-th unit, groups consecutively (longest causal
+  // range first).  Units are numbered sequence-major in order of causal work.
   const int n_groups = (max_q_len + kGroupTokens - 1) / kGroupTokens;
   const int wg = blockIdx.x;
   const int xk = wg / kXcds;
   const int unit = (xk / n_groups) * kXcds + wg % kXcds;
   const int gx = xk % n_groups;
   if (unit >= batch * num_kv_heads) return;  // padding of the last round: uniform
-  const int s = unit / num_kv_heads;
-  const int kvh = unit % num_kv_heads;
   const int tid = threadIdx.x;
+  // Units in order of their sequence's causal work, largest first (up to kSortedBatch
+  // sequences; sequence order past that), so the last workgroups an XCD starts are short.
+  const int s = sequence_by_work(unit / num_kv_heads, cu_q, ctx_lens, batch, total_q, tid);
+  const int kvh = unit % num_kv_heads;
   const bool first = gx == 0 && kvh == 0 && tid == 0;
   const Chunk ch = chunk_of(cu_q, ctx_lens, s, total_q, max_q_len, W * kBlockTokens, first);
   const int groups = (ch.len + kGroupTokens - 1) / kGroupTokens;
