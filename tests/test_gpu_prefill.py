@@ -72,8 +72,8 @@ def test_long_prompts(kv_dtype):
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
 def test_contexts_across_id_windows(kv_dtype):
-    """The LDS kernel reads block ids 256 at a time: contexts of more than 4096 tokens
-    cross that window, with the chunk inside the second window or across the boundary."""
+    """Contexts past 4096 tokens (256 blocks; the fp32 path fetches block ids in windows),
+    with the chunk past that mark or across it."""
     lens = [5200, 4200, 4111]
     chunks = [100, 37, 200]
     say(f"prefill id windows {kv_dtype}")
@@ -81,6 +81,23 @@ def test_contexts_across_id_windows(kv_dtype):
     want = pp.paged_prefill(q, case.k_pool[0], case.v_pool[0], case.block_tables, cu,
                             case.context_lens, case.scale, kv_dtype)
     assert_parity(_run(case, q, cu), want, kv_dtype, f"prefill id windows {kv_dtype}")
+    assert_no_device_error()
+
+
+@pytest.mark.parametrize("batch", [256, 300])
+def test_many_sequences_in_work_order(batch):
+    """The bf16 kernel launches its (sequence, KV head) units largest causal work first,
+    ranking up to 256 sequences per call in LDS (ties by index; the lengths repeat so that
+    many tie) and keeping sequence order past that: every sequence is attended once, at
+    256 (ranked) and 300 (sequence order)."""
+    rng = np.random.default_rng(batch)
+    lens = rng.choice([1, 2, 7, 16, 17, 40], size=batch).astype(int).tolist()
+    chunks = [int(rng.integers(0, n + 1)) for n in lens]
+    say(f"prefill {batch} sequences")
+    case, q, cu = _case(lens, chunks, 8, 2, 64, "bf16", seed=batch)
+    want = pp.paged_prefill(q, case.k_pool[0], case.v_pool[0], case.block_tables, cu,
+                            case.context_lens, case.scale, "bf16")
+    assert_parity(_run(case, q, cu), want, "bf16", f"prefill {batch} sequences")
     assert_no_device_error()
 
 
