@@ -20,6 +20,7 @@ kernel alone, timed with HIP events on the stream it runs on.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -305,11 +306,12 @@ def run_replay(args, np, torch, pkv):
     for t in range(steps):
         active = [s for s in range(B) if t < int(sched.gen_lens[s])]
         plan.append(active)
-        q_all.append([torch.from_numpy(replay_step_values(sched, t, l, active, "q")).cuda()
-                      for l in range(L)])
-        kv_all.append([tuple(torch.from_numpy(x).cuda()
-                             for x in replay_step_values(sched, t, l, active, "kv"))
-                       for l in range(L)])
+        # the step's layers stacked: q [L, n, hq, d], new K and V [L, n, hkv, d]
+        q_all.append(torch.from_numpy(np.stack(
+            [replay_step_values(sched, t, l, active, "q") for l in range(L)])).cuda())
+        kv = [replay_step_values(sched, t, l, active, "kv") for l in range(L)]
+        kv_all.append(tuple(torch.from_numpy(np.stack([x[i] for x in kv])).cuda()
+                            for i in range(2)))
     bm = pkv.BlockManager(nb, bs, free_order=sched.free_order)
     ids = [bm.add_sequence() for _ in range(B)]
     for s in range(B):
@@ -332,8 +334,16 @@ def run_replay(args, np, torch, pkv):
     prompt = np.asarray(sched.prompt_lens, np.int32)
     gen = np.asarray(sched.gen_lens, np.int32)
     ones = np.ones(B, np.int32)
-    # one host buffer per step: tables [n, W], start [n], ctx [n], cu [n + 1]
-    host = np.empty(B * W + 3 * B + 1, np.int32)
+    # a step's tables [n, W], start [n], ctx [n] and cu [n + 1] go up in one copy, from two
+    # pinned host buffers in turn into two device buffers in turn.  The copy is queued
+    # behind the previous step's launches instead of waiting for them (a copy from pageable
+    # memory would), so the host prepares step t + 1 while the GPU runs step t.  A host
+    # buffer is rewritten only after the copy that last read it has run (its event).
+    m_max = B * W + 3 * B + 1
+    stage = [torch.empty(m_max, dtype=torch.int32).pin_memory() for _ in range(2)]
+    stage_np = [x.numpy() for x in stage]
+    stage_dev = [torch.empty(m_max, dtype=torch.int32, device="cuda") for _ in range(2)]
+    stage_ev = [torch.cuda.Event() for _ in range(2)]
     t0 = time.perf_counter()
     ev0.record()
     for t in range(steps):
@@ -341,25 +351,31 @@ def run_replay(args, np, torch, pkv):
         n = len(active)
         act = np.asarray(active, np.intp)
         pos = prompt[act] + t
+        i = t & 1
+        stage_ev[i].synchronize()
+        host = stage_np[i]
         # every sequence's next slot made writable and the tables written in one call
         bm.prepare_step(seq_ids[act], pos, ones[:n], W, tables_out=host[:n * W].reshape(n, W))
         host[n * W:n * W + n] = pos
         host[n * W + n:n * W + 2 * n] = pos + 1
         host[n * W + 2 * n:n * W + 3 * n + 1] = np.arange(n + 1, dtype=np.int32)
-        dev_all = torch.from_numpy(host[:n * W + 3 * n + 1]).cuda()
+        m = n * W + 3 * n + 1
+        dev_all = stage_dev[i][:m]
+        dev_all.copy_(stage[i][:m], non_blocking=True)
+        stage_ev[i].record()
         d_tables = dev_all[:n * W].view(n, W)
         d_start = dev_all[n * W:n * W + n]
         d_ctx = dev_all[n * W + n:n * W + 2 * n]
         d_cu = dev_all[n * W + 2 * n:]
         max_ctx = int(pos.max()) + 1
-        # one work plan for the step, then one append + decode launch per layer
-        step = pkv.DecodeStep(q_all[t][0], kc[0], vc[0], *kv_all[t][0], d_tables, d_start,
-                              d_cu, d_ctx, max_ctx, partition_size=0, out=out[:n],
+        # one work plan for the step, then one append + decode launch per layer, all
+        # layers issued by one library call
+        k_new, v_new = kv_all[t]
+        step = pkv.DecodeStep(q_all[t][0], kc[0], vc[0], k_new[0], v_new[0], d_tables,
+                              d_start, d_cu, d_ctx, max_ctx, partition_size=0, out=out[:n],
                               want_lse=False, workspace=ws)
-        for l in range(L):
-            k, v = kv_all[t][l]
-            step.layer(q_all[t][l], kc[l], vc[l], k, v)
-            calls += 1
+        step.layers(q_all[t], kc, vc, k_new, v_new)
+        calls += L
         ctxs = (pos + 1).astype(np.int64)
         total_tokens += L * int(ctxs.sum())
         total_bytes += L * (int(ctxs.sum()) * 2 * hkv * d * 4 + n * (hq * d * 4 * 2 + 4) +
@@ -385,7 +401,7 @@ def run_replay(args, np, torch, pkv):
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
                    "num_blocks": nb, "steps": steps,
                    "step": "host block manager + table upload + work plan, then per layer one "
-                           "append + decode launch"},
+                           "append + decode launch, every layer issued by one library call"},
         "pct_of_hbm_peak": round(100 * total_bytes / wall / 1e9 / HBM_PEAK_GBPS, 3),
         "seq_tokens_per_s": round(total_tokens / wall, 1),
         "gpu_event_seconds": round(gpu_s, 5),
@@ -469,6 +485,10 @@ def run_crossover(args, np, torch, pkv):
 
 def main():
     args = parse_args()
+    # No cyclic garbage collection in this process: a full collection traverses every
+    # tensor and array made while building the inputs (about 40 ms on the replay's), and
+    # would land inside one timed step at random.  Reference counting frees the rest.
+    gc.disable()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this decode path has no "
               "multi-GPU mode; sharding by sequence or KV head needs no collective.",
@@ -524,9 +544,9 @@ def main():
             x = x.view(np.int16)
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
-    qs = [to_dev(case.q[l]) for l in range(layers)]
-    kcs = [to_dev(case.k_pool[l]) for l in range(layers)]
-    vcs = [to_dev(case.v_pool[l]) for l in range(layers)]
+    # every layer's q and caches stacked on a leading layer dimension; qs[l] etc. are views
+    q_st, kc_st, vc_st = (to_dev(x[:layers]) for x in (case.q, case.k_pool, case.v_pool))
+    qs, kcs, vcs = list(q_st), list(kc_st), list(vc_st)
     q, kc, vc = qs[0], kcs[0], vcs[0]
     tables = to_dev(case.block_tables)
     ctx = to_dev(case.context_lens)
@@ -562,16 +582,19 @@ def main():
                                    (args.append_in_pass == "auto" and layers > 1))
     if in_pass:
         step_plan = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        # each layer appends this step's token rows to its own cache: the rows stacked
+        # per layer for the one-call form
+        kn_st, vn_st = (x.expand(layers, *x.shape).contiguous() for x in (k_new, v_new))
 
     def step():
         if in_pass:
             # lengths advance once per step, so one plan serves every layer: the step-wide
-            # tensors are checked and planned once, then each layer is one checked launch
+            # tensors are checked and planned once, then one library call launches every
+            # layer's append + decode
             ds = pkv.DecodeStep(qs[0], kcs[0], vcs[0], k_new, v_new, tables, start, cu, ctx,
                                 max_ctx, scale=scale, partition_size=P, out=out, lse=lse,
                                 workspace=step_plan)
-            for l in range(layers):
-                ds.layer(qs[l], kcs[l], vcs[l], k_new, v_new)
+            ds.layers(q_st, kc_st, vc_st, kn_st, vn_st)
             return
         for l in range(layers):
             if shared_path:

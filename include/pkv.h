@@ -301,6 +301,30 @@ int pkv_append_paged_decode_planned(float* out, float* lse, const void* q, void*
                                     size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
 
 /*
+ * Every layer of one decode step in one call: for l = 0 .. num_layers - 1,
+ * exactly pkv_append_paged_decode_planned on layer l's tensors, in order, with
+ * the same results and errors (the first failing layer's code is returned and
+ * the later layers are not launched).  Layer l's tensors start at the first
+ * layer's pointer plus l times its layer stride, in elements: out and lse
+ * (float; stride 0 lets every layer write one buffer), q, k_cache / v_cache
+ * (one stride for both) and k_new / v_new (one stride), in the cache dtype.
+ * Everything else (tables, positions, lengths, the plan in `workspace`) is
+ * shared by the layers, as in one step of a model (spindle, "Two bugs worth
+ * recording": lengths advance once per step).  For callers that issue a
+ * step's layers back to back: one host call instead of num_layers.
+ */
+int pkv_append_paged_decode_planned_layers(
+    int32_t num_layers, float* out, int64_t out_layer_stride, float* lse,
+    int64_t lse_layer_stride, const void* q, int64_t q_layer_stride, void* k_cache,
+    void* v_cache, int64_t cache_layer_stride, const void* k_new, const void* v_new,
+    int64_t new_layer_stride, const int32_t* block_tables, int64_t bt_stride,
+    const int32_t* start_pos, const int32_t* cu_new_tokens, int32_t total_new,
+    const int32_t* context_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+    pkv_stream_t stream);
+
+/*
  * Decode for a batch holding copy-on-write fork groups (spindle, "Paging":
  * forked sequences share blocks through reference counts).  Computes the
  * same out and lse as pkv_paged_decode (equal within rounding; the shared

@@ -69,6 +69,10 @@ SIGNATURES = {
                                                        _i64, _vp, _vp, _i32, _vp, _i32, _i32,
                                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                                        _vp, _sz, _i32, _vp]),
+    "pkv_append_paged_decode_planned_layers": (ctypes.c_int, [
+        _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+        _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
+        _vp]),
     "pkv_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                                       _vp, _i32, _i32, _i32, _i32, _i32, _i32,

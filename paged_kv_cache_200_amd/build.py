@@ -26,7 +26,7 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["paged_decode.hip", "prefill.hip", "kv_append.hip", "copy_blocks.hip",
                "status.hip", "static_scratch.hip"]
-HOST_SOURCES = ["block_manager.cpp", "replay.cpp"]
+HOST_SOURCES = ["block_manager.cpp", "replay.cpp", "decode_layers.cpp"]
 
 
 def _hipcc() -> str:

@@ -415,6 +415,39 @@ class DecodeStep:
                             k_new.data_ptr(), v_new.data_ptr(), *self._fixed, s.cuda_stream))
         return out, lse
 
+    def layers(self, q, k_cache, v_cache, k_new, v_new, out=None, lse=None):
+        """Every layer of the step in one library call
+        (pkv_append_paged_decode_planned_layers): the tensors stack the layers on a
+        leading dimension (q [L, *q], caches [L, *cache], new K/V [L, *new], each layer
+        shaped like the first layer's); outputs go to out / lse stacked the same way, or
+        to the bound out / lse, which every layer then overwrites.  Same results as
+        layer() on each slice in order; returns (out, lse)."""
+        kinds = self._kinds
+        L = q.shape[0] if isinstance(q, torch.Tensor) and q.dim() > 0 else -1
+        self._check(q, (L,) + tuple(self._q_shape), kinds, "q")
+        self._check(k_cache, (L,) + tuple(self._cache_shape), kinds, "k_cache")
+        self._check(v_cache, (L,) + tuple(self._cache_shape), kinds, "v_cache")
+        self._check(k_new, (L,) + tuple(self._new_shape), kinds, "k_new")
+        self._check(v_new, (L,) + tuple(self._new_shape), kinds, "v_new")
+        out_stride, lse_stride = 0, 0
+        if out is None:
+            out = self.out
+        else:
+            self._check(out, (L,) + tuple(self._out_shape), (torch.float32,), "out")
+            out_stride = out.stride(0)
+        if lse is None:
+            lse = self.lse
+        else:
+            self._check(lse, (L,) + tuple(self._lse_shape), (torch.float32,), "lse")
+            lse_stride = lse.stride(0)
+        s = torch.cuda.current_stream() if self.stream is None else self.stream
+        _lib.call("pkv_append_paged_decode_planned_layers", L, out.data_ptr(), out_stride,
+                  None if lse is None else lse.data_ptr(), lse_stride, q.data_ptr(),
+                  q.stride(0), k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(0),
+                  k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), *self._fixed,
+                  s.cuda_stream)
+        return out, lse
+
 
 def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_starts,
                                group_shared_blocks, max_shared_blocks, max_context_len,

@@ -633,6 +633,60 @@ def test_append_in_pass_over_layers_with_one_plan():
     assert after.tobytes() != before  # the other sequences' tokens were written
 
 
+@pytest.mark.parametrize("shape", ["qwen_bf16_P256", "f32_d64_P0"])
+def test_decode_step_layers_in_one_call(shape):
+    """DecodeStep.layers (pkv_append_paged_decode_planned_layers: the step's layers stacked,
+    one library call) leaves every layer's pool, out and lse equal to one layer() call per
+    layer, bit for bit, with stacked outputs and with the bound one (the last layer's
+    result); a stack whose layers do not match the first layer's is refused."""
+    say(f"decode step layers: {shape}")
+    if shape == "qwen_bf16_P256":
+        case, P = config_case("qwen_gqa", 3, layers=4, max_batch=24), 256
+    else:
+        case = build_case("layers", [1, 16, 17, 300, 190, 33, 64, 2], 12, 12, 64, "f32",
+                          seed=9, layers=4)
+        P = 0
+    ops = _ops()
+    B, L = case.batch, 4
+    conv = bf16_bits if case.kv_dtype == "bf16" else (lambda x: x)
+    rng = np.random.default_rng(L)
+    dims = (L, B, case.num_kv_heads, case.head_dim)
+    kn = dev(conv(rng.standard_normal(dims).astype(np.float32)))
+    vn = dev(conv(rng.standard_normal(dims).astype(np.float32)))
+    start = dev((case.context_lens - 1).astype(np.int32))
+    cu = dev(np.arange(B + 1, dtype=np.int32))
+    tables, ctx = dev(case.block_tables), dev(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    q = dev(np.stack([case.q[l] for l in range(L)]))
+    pools = [(dev(np.stack(case.k_pool[:L])), dev(np.stack(case.v_pool[:L]))) for _ in range(3)]
+    steps = [ops.DecodeStep(q[0], pools[i][0][0], pools[i][1][0], kn[0], vn[0], tables, start,
+                            cu, ctx, max_ctx, scale=float(case.scale), partition_size=P)
+             for i in range(3)]
+    outs = torch.empty((L, B, case.num_q_heads, case.head_dim), dtype=torch.float32,
+                       device="cuda")
+    lses = torch.empty((L, B, case.num_q_heads), dtype=torch.float32, device="cuda")
+    ref = []
+    for l in range(L):
+        o, ls = steps[0].layer(q[l], pools[0][0][l], pools[0][1][l], kn[l], vn[l])
+        ref.append((o.clone(), ls.clone()))
+    steps[1].layers(q, pools[1][0], pools[1][1], kn, vn, out=outs, lse=lses)
+    o_last, l_last = steps[2].layers(q, pools[2][0], pools[2][1], kn, vn)
+    torch.cuda.synchronize()
+    for i in (1, 2):
+        assert pools[i][0].cpu().numpy().tobytes() == pools[0][0].cpu().numpy().tobytes(), i
+        assert pools[i][1].cpu().numpy().tobytes() == pools[0][1].cpu().numpy().tobytes(), i
+    for l in range(L):
+        assert outs[l].cpu().numpy().tobytes() == ref[l][0].cpu().numpy().tobytes(), l
+        assert lses[l].cpu().numpy().tobytes() == ref[l][1].cpu().numpy().tobytes(), l
+    assert o_last.cpu().numpy().tobytes() == ref[-1][0].cpu().numpy().tobytes()
+    assert l_last.cpu().numpy().tobytes() == ref[-1][1].cpu().numpy().tobytes()
+    assert_no_device_error()
+    with pytest.raises(ValueError):
+        steps[1].layers(q[:, :-1], pools[1][0], pools[1][1], kn, vn)
+    with pytest.raises(ValueError):
+        steps[1].layers(q, pools[1][0][:3], pools[1][1], kn, vn)
+
+
 @pytest.mark.parametrize("shape", ["qwen_bf16_P256", "f32_d128_P0"])
 def test_decode_step_equals_planned_calls(shape):
     """DecodeStep (step-wide tensors bound and planned once, one layer() per layer) leaves
