@@ -459,8 +459,12 @@ int pkv_paged_decode_planned(float* out, float* lse, const void* q, const void* 
  * For each (s, h), over p < ceil(context_lens[s] / partition_size) with
  * part_lse > -inf:  M = max lse_p, w_p = exp(lse_p - M),
  *   out = sum w_p part_out_p / sum w_p,  lse = M + ln sum w_p;
- * no live partition gives out = 0, lse = -inf.  Layouts as in
- * pkv_paged_decode_partials.  lse may be NULL.
+ * no live partition gives out = 0, lse = -inf.  Rounding order: a row of 9 to
+ * 64 partitions is merged in two steps, each group of 8 consecutive
+ * partitions by the formula above, then the group results by the same
+ * formula (the same value in exact arithmetic); other rows in one step.  A
+ * call with max_partitions from 9 to 64 runs one workgroup per row, one wave
+ * per group.  Layouts as in pkv_paged_decode_partials.  lse may be NULL.
  */
 int pkv_lse_combine(float* out, float* lse, const float* part_out, const float* part_lse,
                     const int32_t* context_lens, int32_t batch, int32_t num_q_heads,

@@ -81,34 +81,118 @@ __device__ __forceinline__ float load_partial(const float* p) {
 #ifndef PKV_IN_PASS_MERGE_MAX
 #define PKV_IN_PASS_MERGE_MAX 8
 #endif
-#ifndef PKV_IN_PASS_MERGE_CHUNK
-#define PKV_IN_PASS_MERGE_CHUNK 8
-#endif
 constexpr int kMaxInPassMergeSlots = PKV_IN_PASS_MERGE_MAX;
-constexpr int kInPassMergeChunk = PKV_IN_PASS_MERGE_CHUNK;
 
-// kChunk: partitions whose partial outputs are loaded together, before their weighted
-// sum (32 in the combine kernel; 8 in the merge inside the first pass).  The sum runs over
-// the partitions in order whatever the chunk (a chunk's slots past the last partition add
-// 0), so both give the same bits.
-template <int D, bool kAgent = false, int kChunk = 32>
+// The combine merges a row of more than kMaxInPassMergeSlots partitions, up to
+// kMergeGroups groups of kMaxInPassMergeSlots consecutive partitions, in two steps: each
+// group into one result, then the groups (the same identity, applied twice).  The groups
+// of a row then run on waves of their own (lse_combine_grouped_kernel).  Longer rows are
+// merged in one step.
+constexpr int kMergeGroups = kMaxInPassMergeSlots;
+constexpr int kMaxTwoLevelSlots = kMergeGroups * kMaxInPassMergeSlots;
+
+__host__ __device__ constexpr int merge_group_count(int slots) {
+  return (slots + kMaxInPassMergeSlots - 1) / kMaxInPassMergeSlots;
+}
+
+// One merge step over at most kMaxInPassMergeSlots results: lane u < n holds result u's
+// log-sum-exp (-inf on the other lanes) and x[u] that result's D/64 output dims of this
+// lane (0 past n).  The weighted sum runs over the results in order.
+template <int kPer>
+__device__ __forceinline__ void merge_step(float lp, const float (&x)[kMaxInPassMergeSlots][kPer],
+                                           float (&o)[kPer], float& ls) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const float M = wave_max(lp);
+  const float w = lp == -INFINITY ? 0.0f : fast_exp2((lp - M) * kLog2e);
+  const float den = wave_sum(w);
+  float acc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kMaxInPassMergeSlots; ++u) {
+    const float wp = __shfl(w, u);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) acc[j] = fmaf(wp, x[u][j], acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) o[j] = den > 0.0f ? acc[j] / den : 0.0f;
+  ls = den > 0.0f ? M + __logf(den) : -INFINITY;
+}
+
+// Group g (partitions g * kMaxInPassMergeSlots ..) of a row of nparts partitions, merged
+// by one wave into o (this lane's dims) and ls.
+template <int D>
+__device__ __forceinline__ void merge_group(const float* __restrict__ pl,
+                                            const float* __restrict__ po, int nparts, int g,
+                                            int lane, float (&o)[D / kWave], float& ls) {
+  constexpr int kS = kMaxInPassMergeSlots;
+  constexpr int kPer = D / kWave;
+  const int p0 = g * kS;
+  const int cnt = min(kS, nparts - p0);
+  const float lp = lane < cnt ? pl[p0 + lane] : -INFINITY;
+  float x[kS][kPer];
+#pragma unroll
+  for (int u = 0; u < kS; ++u)
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) x[u][j] = u < cnt ? po[(p0 + u) * D + j * kWave + lane] : 0.0f;
+  merge_step<kPer>(lp, x, o, ls);
+}
+
+// The combine of one (sequence, head) row by one wave.  Up to kMaxInPassMergeSlots
+// partitions: one merge step, the arithmetic of the first pass's own merge, so both give
+// the same bits.  Up to kMaxTwoLevelSlots: two steps (groups, then the groups).  Longer
+// rows: one step over all partitions, kChunk partitions' outputs loaded together.
+template <int D, int kChunk = 32>
 __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* __restrict__ lse_el,
                                             const float* __restrict__ pl,
                                             const float* __restrict__ po, int nparts, int lane) {
   constexpr int kPer = D / kWave;  // output dims per lane
   constexpr float kLog2e = 1.44269504088896340736f;
-  // Up to 64 partitions the log-sum-exps are loaded once, for the max and the weights.
-  const float lp0 = lane < nparts ? load_partial<kAgent>(pl + lane) : -INFINITY;
+  if (nparts <= kMaxInPassMergeSlots) {
+    // one step, every load issued before the first wait (as in the first pass's merge)
+    float o[kPer], ls;
+    merge_group<D>(pl, po, nparts, 0, lane, o, ls);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) out_row[j * kWave + lane] = o[j];
+    if (lse_el != nullptr && lane == 0) *lse_el = ls;
+    return;
+  }
+  if (nparts <= kMaxTwoLevelSlots) {
+    // two steps: lane g ends up with group g's log-sum-exp, go[g] with its dims
+    const int ng = merge_group_count(nparts);
+    float gl = -INFINITY;
+    float go[kMergeGroups][kPer];
+#pragma unroll
+    for (int g = 0; g < kMergeGroups; ++g) {
+      if (g < ng) {
+        float ls;
+        merge_group<D>(pl, po, nparts, g, lane, go[g], ls);
+        if (lane == g) gl = ls;
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) go[g][j] = 0.0f;
+      }
+    }
+    float o[kPer], ls;
+    merge_step<kPer>(gl, go, o, ls);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) out_row[j * kWave + lane] = o[j];
+    if (lse_el != nullptr && lane == 0) *lse_el = ls;
+    return;
+  }
+  // One step over every partition: the max of the log-sum-exps (64 per wave load), then
+  // the weights and the weighted sum in chunks.
+  const float lp0 = lane < nparts ? pl[lane] : -INFINITY;
   float M = wave_max(lp0);
   for (int p0 = kWave; p0 < nparts; p0 += kWave)
-    M = fmaxf(M, wave_max(p0 + lane < nparts ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY));
+    M = fmaxf(M, wave_max(p0 + lane < nparts ? pl[p0 + lane] : -INFINITY));
   float acc[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) acc[j] = 0.0f;
   float den = 0.0f;
   for (int p0 = 0; p0 < nparts; p0 += kWave) {
     const int cnt = min(kWave, nparts - p0);
-    const float lp = p0 == 0 ? lp0 : lane < cnt ? load_partial<kAgent>(pl + p0 + lane) : -INFINITY;
+    const float lp = p0 == 0 ? lp0 : lane < cnt ? pl[p0 + lane] : -INFINITY;
     const float w = (lp == -INFINITY) ? 0.0f : fast_exp2((lp - M) * kLog2e);
     den += wave_sum(w);
     // kChunk partitions' loads in flight at a time; past the last partition the weight is
@@ -122,7 +206,7 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
         wp[u] = __shfl(w, (p + u) % kWave);
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-          x[u][j] = live ? load_partial<kAgent>(po + (p0 + p + u) * D + j * kWave + lane) : 0.0f;
+          x[u][j] = live ? po[(p0 + p + u) * D + j * kWave + lane] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < kChunk; ++u)
@@ -139,8 +223,19 @@ __device__ __forceinline__ void combine_row(float* __restrict__ out_row, float* 
 // workgroup.
 constexpr int kCombineWaves = 4;
 
-// nslots (nullable): per sequence, the number of slots to merge, 0 when the first pass
-// wrote the sequence's result itself; without it the count follows from the length.
+// Partitions to merge for sequence s, 0 when there is nothing to do.  nslots (nullable):
+// per sequence, the number of slots to merge, 0 when the first pass wrote the sequence's
+// result itself; without it the count follows from the length.
+__device__ __forceinline__ int combine_parts(int s, const int32_t* __restrict__ ctx_lens,
+                                             const int32_t* __restrict__ nslots, int cap,
+                                             int part_tokens, int max_parts, int skip_single) {
+  if (nslots != nullptr) return max(0, min(nslots[s], max_parts));
+  int n = ctx_lens[s];
+  n = n < 0 ? 0 : min(n, cap);
+  const int nparts = min(n > 0 ? (n + part_tokens - 1) / part_tokens : 1, max_parts);
+  return skip_single && nparts == 1 ? 0 : nparts;
+}
+
 template <int D>
 __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
     float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
@@ -150,21 +245,65 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
   const int row = blockIdx.x * kCombineWaves + threadIdx.x / kWave;  // (s, h) flattened
   const int lane = threadIdx.x % kWave;
   if (row >= batch * num_q_heads) return;
-  const int s = row / num_q_heads;
-  int nparts;
-  if (nslots != nullptr) {
-    nparts = min(nslots[s], max_parts);
-    if (nparts <= 0) return;
-  } else {
-    int n = ctx_lens[s];
-    n = n < 0 ? 0 : min(n, cap);
-    nparts = n > 0 ? (n + part_tokens - 1) / part_tokens : 1;
-    nparts = min(nparts, max_parts);
-    if (skip_single && nparts == 1) return;
-  }
+  const int nparts = combine_parts(row / num_q_heads, ctx_lens, nslots, cap, part_tokens,
+                                   max_parts, skip_single);
+  if (nparts <= 0) return;
   const size_t sh = static_cast<size_t>(row);
   combine_row<D>(out + sh * D, lse != nullptr ? lse + sh : nullptr, part_lse + sh * max_parts,
                  part_out + sh * max_parts * D, nparts, lane);
+}
+
+// The combine when no row has more than kMaxTwoLevelSlots partitions: one workgroup of
+// kMergeGroups waves per (sequence, query head).  A row of more than
+// kMaxInPassMergeSlots partitions has wave g merge group g, then wave 0 merge the groups
+// through LDS: the steps of combine_row, so the same bits, with the groups' loads in
+// flight on several waves at once.  Shorter rows are combine_row on wave 0.
+template <int D>
+__global__ __launch_bounds__(kMergeGroups * kWave) void lse_combine_grouped_kernel(
+    float* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_out,
+    const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ nslots, int batch, int cap, int num_q_heads, int part_tokens,
+    int max_parts, int skip_single) {
+  constexpr int kPer = D / kWave;
+  __shared__ float s_o[kMergeGroups][D];
+  __shared__ float s_l[kMergeGroups];
+  const int row = blockIdx.x;  // (s, h) flattened; the grid has batch * num_q_heads
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int nparts = combine_parts(row / num_q_heads, ctx_lens, nslots, cap, part_tokens,
+                                   max_parts, skip_single);
+  if (nparts <= 0) return;
+  const size_t sh = static_cast<size_t>(row);
+  const float* pl = part_lse + sh * max_parts;
+  const float* po = part_out + sh * max_parts * D;
+  if (nparts <= kMaxInPassMergeSlots) {
+    if (wave == 0) combine_row<D>(out + sh * D, lse != nullptr ? lse + sh : nullptr, pl, po,
+                                  nparts, lane);
+    return;
+  }
+  const int ng = merge_group_count(nparts);
+  if (wave < ng) {
+    float o[kPer], ls;
+    merge_group<D>(pl, po, nparts, wave, lane, o, ls);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) s_o[wave][j * kWave + lane] = o[j];
+    if (lane == 0) s_l[wave] = ls;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float gl = lane < ng ? s_l[lane] : -INFINITY;
+    float go[kMergeGroups][kPer];
+#pragma unroll
+    for (int u = 0; u < kMergeGroups; ++u)
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) go[u][j] = u < ng ? s_o[u][j * kWave + lane] : 0.0f;
+    float o[kPer], ls;
+    merge_step<kPer>(gl, go, o, ls);
+    float* out_row = out + sh * D;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) out_row[j * kWave + lane] = o[j];
+    if (lse != nullptr && lane == 0) lse[sh] = ls;
+  }
 }
 
 // Grid layouts of the first pass.
@@ -528,6 +667,17 @@ void combine_launch(hipStream_t stream, float* out, float* lse, const float* par
                     const float* part_lse, const int32_t* ctx, const int32_t* nslots, int batch,
                     int cap, int hq, int D, int part_tokens, int max_parts, int skip_single) {
   const int rows = batch * hq;
+  if (max_parts > kMaxInPassMergeSlots && max_parts <= kMaxTwoLevelSlots) {
+    if (D == 64)
+      hipLaunchKernelGGL(lse_combine_grouped_kernel<64>, dim3(rows), dim3(kMergeGroups * kWave), 0,
+                         stream, out, lse, part_out, part_lse, ctx, nslots, batch, cap, hq,
+                         part_tokens, max_parts, skip_single);
+    else
+      hipLaunchKernelGGL(lse_combine_grouped_kernel<128>, dim3(rows), dim3(kMergeGroups * kWave),
+                         0, stream, out, lse, part_out, part_lse, ctx, nslots, batch, cap, hq,
+                         part_tokens, max_parts, skip_single);
+    return;
+  }
   const dim3 grid((rows + kCombineWaves - 1) / kCombineWaves);
   if (D == 64)
     hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineWaves * kWave), 0, stream, out,

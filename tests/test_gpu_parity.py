@@ -416,14 +416,65 @@ def test_decode_equals_partials_plus_combine_bitwise(P):
     ("f32", 8, 2, 128, [700, 5, 256, 129], 128),                # 6 slots
     ("bf16", 32, 8, 128, [1024, 1023, 897, 9, 600], 128),       # 8 slots: the in-pass limit
     ("bf16", 32, 8, 128, [1152, 1151, 1025, 9, 600], 128),      # 9 slots: the combine launch
+    ("bf16", 32, 8, 128, [2176, 2049, 600, 9], 128),            # 17: a last group of one
+    ("bf16", 14, 2, 64, [2200, 1, 513, 40], 128),               # 18, matrix-core pass
+    ("bf16", 32, 8, 128, [1024, 1000, 9], 16),                  # 64: the grouped combine
+    ("f32", 12, 12, 64, [1040, 17, 300], 16),                   # 65: one wave per row
 ])
 def test_decode_equals_partials_plus_combine_shapes(kv_dtype, hq, hkv, d, lens, P):
     """The merge of split sequences, inside the first pass up to 8 partitions and in the
-    combine kernel past that, equals the first pass's partials + the standalone combine,
-    bit for bit, for every head shape it is compiled for here."""
+    combine kernel past that (two steps from 9 to 64 partitions), equals the first pass's
+    partials + the standalone combine, bit for bit, for every head shape it is compiled
+    for here; and the oracle's result within tolerance."""
     case = build_case("merge", lens, hq, hkv, d, kv_dtype, seed=len(lens) + P)
     _check_decode_equals_partials_plus_combine(case, P)
     assert_parity(run_decode(DeviceCase(case), P), oracle_decode(case), kv_dtype, f"merge P{P}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_combine_in_two_steps_on_either_kernel(d):
+    """Rows of 9 to 64 partitions are merged in two steps (each group of 8 consecutive
+    partitions, then the groups).  A call whose max_partitions is at most 64 runs them on
+    one wave per group (lse_combine_grouped_kernel), a wider call on one wave per row:
+    the same partials give the same bits either way, and the oracle's combine within
+    float32 rounding.  Slots past a row's count hold NaN and must not be read; empty
+    partitions (lse -inf) and an all-empty row are included."""
+    say(f"combine in two steps, d {d}")
+    ops = _ops()
+    P, hq = 16, 3
+    counts = [1, 5, 8, 9, 16, 17, 33, 63, 64, 40]
+    B = len(counts)
+    ctx = np.array([n * P - (n % 3) for n in counts], np.int32)
+    rng = np.random.default_rng(d)
+    po = rng.standard_normal((B, hq, 64, d)).astype(np.float32)
+    pl = rng.uniform(-6.0, 6.0, (B, hq, 64)).astype(np.float32)
+    pl[2, 0, 3] = -np.inf            # one empty partition in an 8-slot row
+    pl[4, 1, :7] = -np.inf           # a whole first group empty
+    pl[9, 2, :40] = -np.inf          # a row with nothing live
+    for s, n in enumerate(counts):
+        po[s, :, n:] = np.nan
+        pl[s, :, n:] = np.nan
+    wide_o = np.full((B, hq, 80, d), np.nan, np.float32)
+    wide_l = np.full((B, hq, 80), np.nan, np.float32)
+    wide_o[:, :, :64], wide_l[:, :, :64] = po, pl
+    dctx = dev(ctx)
+    o1, l1 = ops.lse_combine(dev(po), dev(pl), dctx, P)
+    o2, l2 = ops.lse_combine(dev(wide_o), dev(wide_l), dctx, P)
+    torch.cuda.synchronize()
+    assert o1.cpu().numpy().tobytes() == o2.cpu().numpy().tobytes()
+    assert l1.cpu().numpy().tobytes() == l2.cpu().numpy().tobytes()
+    ref_l = pl.astype(np.float64)
+    ref_o = np.nan_to_num(po.astype(np.float64))
+    for s, n in enumerate(counts):
+        ref_l[s, :, n:] = -np.inf
+    want = pa.combine_partitions(ref_o, ref_l)
+    got = (o1.cpu().numpy(), l1.cpu().numpy())
+    assert np.array_equal(np.isneginf(got[1]), np.isneginf(want[1]))
+    assert np.all(got[0][9, 2] == 0.0)
+    assert np.max(np.abs(got[0] - want[0])) < 1e-5
+    live = ~np.isneginf(want[1])
+    assert np.max(np.abs(got[1][live] - want[1][live])) < 1e-5
+    assert_no_device_error()
 
 
 def _check_decode_equals_partials_plus_combine(case, P):
