@@ -67,6 +67,10 @@ def parse_args():
                    help="split-KV partition size in tokens (default: the workload's own, else "
                         "1024 for fork groups on the shared-prefix path, else 4096)")
     p.add_argument("--kernel-reps", type=int, default=50)
+    p.add_argument("--settle-seconds", type=float, default=0.3,
+                   help="before the warmup steps, run steps (untimed) for this long: the GPU's "
+                        "clocks take a few hundred ms of load to settle, far longer than a few "
+                        "0.2 ms warmup steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time for the oracle baseline (repeats the whole batch)")
@@ -99,6 +103,15 @@ def parse_args():
                    help="before the timed steps, run 3 device copies of MIB MiB (a known-size "
                         "reference for HBM traffic counters)")
     return p.parse_args()
+
+
+def settle(fn, torch, seconds):
+    """Run fn, untimed, until `seconds` of wall time have passed."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def algorithmic_bytes(case, append_tokens: int):
@@ -222,6 +235,7 @@ def run_prefill(args, np, torch, pkv):
         pkv.kv_append(kc, vc, k_new, v_new, tables, start, cu)
         prefill()
 
+    settle(step, torch, args.settle_seconds)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -260,6 +274,7 @@ def run_prefill(args, np, torch, pkv):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_seconds,
         "ms_per_step": round(step_s * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -638,6 +653,7 @@ def main():
         run = graph.replay
 
     print("[bench] warmup", file=sys.stderr, flush=True)
+    settle(run, torch, args.settle_seconds)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -664,18 +680,28 @@ def main():
         torch.cuda.synchronize()
         per_step = np.array([e0.elapsed_time(e1) for e0, e1 in marks])
         ms_per_step = float(np.mean(per_step))
+        wall = time.perf_counter() - t0
         del scratch
     else:
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        # the K steps between two events only: an event recorded after every step added
+        # 2.3-3.5 us to each ~227 us step of the headline workload
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / args.steps
+        wall = time.perf_counter() - t0
+        # the spread of single steps, from a second run of K steps with an event after each
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         evs[0].record(stream)
         for i in range(args.steps):
             run()
             evs[i + 1].record(stream)
         torch.cuda.synchronize()
         per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
-        ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
-    wall = time.perf_counter() - t0
     print(f"[bench] {args.steps} steps{' (cold)' if args.cold else ''}: "
           f"{ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
@@ -763,6 +789,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_seconds,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
