@@ -804,6 +804,7 @@ __device__ __forceinline__ int unit_slot(const SeqUnits& u, int p) {
 // Group starts are searched in an LDS copy when they fit (one load wave instead of a
 // chain of dependent global loads per sequence).
 constexpr int kPlanLdsGroups = 2047;
+constexpr int kPlanLaneRun = 16;
 
 __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restrict__ plan_count,
                                            int* __restrict__ nslots, const PlanInput in) {
@@ -854,9 +855,30 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
     }
     const int incl = block_scan_inclusive(s_scan, u.full);
     const int first = s_full_total + incl - u.full;
-    for (int p = 0; p < u.full; ++p) {
+    // The full partitions' entries.  A thread stores its sequence's when they are few; a
+    // sequence with more than kPlanLaneRun (64 for 32768 tokens at P = 512: one thread
+    // storing them in a row was the plan's longest chain) has them stored by every lane
+    // of the wave, one such sequence at a time.  unit_slot(u, p) is unit_slot(u, 0) + p:
+    // the direct flag is only set for a sequence's single unit.
+    const bool own = u.full <= kPlanLaneRun;
+    for (int p = 0; p < (own ? u.full : 0); ++p) {
       const int t0 = u.base + p * P;
       plan[first + p] = make_int4(s, t0, t0 + P, unit_slot(u, p));
+    }
+    {
+      const int lane = tid % kWave;
+      const int slot0 = u.full > 0 ? unit_slot(u, 0) : 0;
+      unsigned long long pending = __ballot(!own);
+      while (pending != 0) {
+        const int j = __builtin_ctzll(pending);
+        pending &= pending - 1;
+        const int sj = __shfl(s, j), fj = __shfl(first, j), nj = __shfl(u.full, j);
+        const int bj = __shfl(u.base, j), slj = __shfl(slot0, j);
+        for (int p = lane; p < nj; p += kWave) {
+          const int t0 = bj + p * P;
+          plan[fj + p] = make_int4(sj, t0, t0 + P, slj + p);
+        }
+      }
     }
     __syncthreads();
     if (tid == kPlanThreads - 1) s_full_total += incl;
