@@ -853,6 +853,10 @@ __device__ __forceinline__ void build_plan(int4* __restrict__ plan, int* __restr
       nslots[s] = (u.nsp == 0 && units == 1) ? 0 : u.nsp + units;
       if (u.tail) atomicAdd(&s_cursor[key_of(u)], 1);
     }
+    if (P == 0) {  // one unit per sequence: no full partitions to place
+      __syncthreads();
+      continue;
+    }
     const int incl = block_scan_inclusive(s_scan, u.full);
     const int first = s_full_total + incl - u.full;
     // The full partitions' entries.  A thread stores its sequence's when they are few; a
