@@ -206,6 +206,16 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
     for (int k = 0; k < kSteps; ++k)
       qr[k] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * k);
   }
+  // The softmax below scales raw scores inside the exponent and scales their max once,
+  // which needs a scale >= 0: a negative one is applied as its magnitude to -q (the sign
+  // flip of a bf16 word is exact, and so is the negated product).
+  float sl2 = scale_log2;
+  if (sl2 < 0.0f) {
+    sl2 = -sl2;
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k)
+      qr[k] = qr[k] ^ u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
   f32x16_t o[kDimTiles];
 #pragma unroll
   for (int dt = 0; dt < kDimTiles; ++dt)
@@ -295,12 +305,16 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
     }
   };
   auto attend = [&](int stage, const f32x16_t& sc, int t_base) {
-    // Scores in log2 units, masked ones -inf (a select, so stale keys' NaN scores drop
-    // out).  The scale is applied before the max, so the max key's weight is exactly 1.
+    // Raw scores, masked ones -inf (a select, so stale keys' NaN scores drop out).  The
+    // max is taken on them and scaled once (rounding is monotonic, so that is the max of
+    // the scaled scores); each weight is exp2(score * scale - m) with the scale inside
+    // the exponent's FMA.  The max key's exponent is then the rounding residual of its
+    // own scaled score, and its weight rounds to exactly 1 in bf16.
     float x[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = sc[e] * scale_log2;
-    if (t_base + kPairTokens > lim0) {
+    for (int e = 0; e < 16; ++e) x[e] = sc[e];
+    const bool masked = t_base + kPairTokens > lim0;  // uniform
+    if (masked) {
       const int lim = n_c - t_base - 4 * h;  // keys 8i + j of the lane below lim are attended
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
     float bm = x[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) bm = fmaxf(bm, x[e]);
-    bm = max_xor32(bm);
+    bm = max_xor32(bm) * sl2;
     const bool raise = bm > m + kLazyMaxSlack;
     if (__any(raise)) {
       float a = 1.0f;
@@ -324,15 +338,19 @@ __global__ __launch_bounds__(kLdsThreads, 3) void prefill_t32_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] *= a;
     }
-    // No select for masked weights: exp2(-inf - m) is 0 once m is finite, and every live
-    // row's m is finite from pair 0 on (it holds token 0, which every causal row attends).
-    // Rows past the chunk's last token keep m = -inf and turn NaN; the products keep rows
+    // Masked weights are set to 0 by a select, in the pairs that have masks only.  Every
+    // live row's m is finite from pair 0 on (it holds token 0, which every causal row
+    // attends); rows past the chunk's last token may turn NaN, the products keep rows
     // (columns of the transposed tiles) apart, and those rows are never written.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[8 * t + e] - m);
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[8 * t + e], sl2, -m));
+      if (masked) {  // a masked key's weight is 0 also at scale 0 (-inf * 0 is NaN)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = x[8 * t + e] == -INFINITY ? 0.0f : p[e];
+      }
       // (The packed words are kept as four scalars: read back as elements of the operand
       // vector, the ROCm 7.2 compiler fed the first word to all four dot products.)
       uint32_t pw[4];

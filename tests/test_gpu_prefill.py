@@ -32,18 +32,34 @@ def _case(lens, chunks, hq, hkv, d, kv_dtype, seed):
     return case, q, cu
 
 
-def _run(case, q, cu, max_q=None):
+def _run(case, q, cu, max_q=None, scale=None):
     from paged_kv_cache_200_amd import ops
     mq = int(np.diff(cu).max(initial=0)) if max_q is None else max_q
     o, l = ops.paged_prefill(dev(q), dev(case.k_pool[0]), dev(case.v_pool[0]),
                              dev(case.block_tables), dev(cu), dev(case.context_lens), mq,
-                             scale=float(case.scale))
+                             scale=float(case.scale) if scale is None else scale)
     torch.cuda.synchronize()
     return o.cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64)
 
 
 SHAPES = [("bf16", 32, 8, 128), ("bf16", 14, 2, 64), ("bf16", 8, 8, 64), ("bf16", 24, 3, 128),
           ("f32", 12, 12, 64), ("f32", 8, 2, 128)]
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
+@pytest.mark.parametrize("kv_dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("bf16", 14, 2, 64)])
+def test_any_scale(kv_dtype, hq, hkv, d, scale):
+    """The matrix-core prefill scales raw scores inside each exponent and scales their max
+    once; a negative scale runs as its magnitude on -q, and at scale 0 (uniform weights
+    over each row's causal range) masked keys still weigh 0."""
+    lens = [1, 17, 64, 100, 333, 40]
+    chunks = [1, 17, 5, 60, 120, 40]
+    say(f"prefill scale {scale} {kv_dtype} {hq}/{hkv}x{d}")
+    case, q, cu = _case(lens, chunks, hq, hkv, d, kv_dtype, seed=hq + d + 5)
+    want = pp.paged_prefill(q, case.k_pool[0], case.v_pool[0], case.block_tables, cu,
+                            case.context_lens, np.float32(scale), kv_dtype)
+    assert_parity(_run(case, q, cu, scale=scale), want, kv_dtype, f"prefill scale {scale}")
+    assert_no_device_error()
 
 
 @pytest.mark.parametrize("kv_dtype,hq,hkv,d", SHAPES)
