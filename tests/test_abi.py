@@ -61,6 +61,19 @@ def test_host_only_calls():
     st = lib.pkv_kv_append(None, None, None, None, None, 1, None, None, 1, 0, 1, 64, 16, 4, 0,
                            None)
     assert st == 0  # nothing to append
+    # a step's layers in one call: its own checks, then each layer's
+    layers = lib.pkv_append_paged_decode_planned_layers
+    args = [None, 0, None, 0, None, 0, None, None, 0, None, None, 0, None, 1, None, None, 1,
+            None, 1, 8, 2, 64, 16, 4, 16, 1.0, 0, None, 0, 1, None]
+    assert layers(0, *args) == 0                      # no layers: nothing to do
+    assert layers(-1, *args) == -3                    # negative layer count
+    bad_stride = list(args)
+    bad_stride[5] = -1                                # q layer stride
+    assert layers(2, *bad_stride) == -3
+    bad_dtype = list(args)
+    bad_dtype[-2] = 7
+    assert layers(2, *bad_dtype) == -2
+    assert layers(2, *args) == -1                     # the first layer's null pointers
 
 
 def test_decode_step_refuses_host_tensors():
