@@ -29,6 +29,29 @@ def test_defaults():
                                                                        None, False, False)
     assert a.append_in_pass == "auto"
     assert a.steps * 0.25e-3 < 60   # the default timed region stays well under a minute
+    assert a.settle_seconds == 0.3  # untimed steps before the warmup: the clocks settle
+
+
+def test_settle_runs_until_its_time_is_up():
+    """settle() runs the step in groups of 8, synchronizing after each group, until the
+    given wall time has passed (and not at all for 0 s)."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    class FakeTorch:
+        class cuda:
+            syncs = 0
+
+            @staticmethod
+            def synchronize():
+                FakeTorch.cuda.syncs += 1
+
+    calls = []
+    bench.settle(lambda: calls.append(1), FakeTorch, 0.0)
+    assert calls == [] and FakeTorch.cuda.syncs == 0
+    bench.settle(lambda: calls.append(1), FakeTorch, 0.02)
+    assert len(calls) >= 8 and len(calls) % 8 == 0
+    assert FakeTorch.cuda.syncs == len(calls) // 8
 
 
 def test_traffic_records_are_consistent():
