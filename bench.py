@@ -385,13 +385,11 @@ def run_replay(args, np, torch, pkv):
         d_ctx = dev_all[n * W + n:n * W + 2 * n]
         d_cu = dev_all[n * W + 2 * n:]
         max_ctx = int(pos.max()) + 1
-        # one work plan for the step, then one append + decode launch per layer, all
-        # layers issued by one library call
+        # one work plan for the step, then one append + decode launch per layer: two
+        # library calls, the step's tensors checked once
         k_new, v_new = kv_all[t]
-        step = pkv.DecodeStep(q_all[t][0], kc[0], vc[0], k_new[0], v_new[0], d_tables,
-                              d_start, d_cu, d_ctx, max_ctx, partition_size=0, out=out[:n],
-                              want_lse=False, workspace=ws)
-        step.layers(q_all[t], kc, vc, k_new, v_new)
+        pkv.append_paged_decode_layers(q_all[t], kc, vc, k_new, v_new, d_tables, d_start, d_cu,
+                                       d_ctx, max_ctx, ws, partition_size=0, out=out[:n])
         calls += L
         ctxs = (pos + 1).astype(np.int64)
         total_tokens += L * int(ctxs.sum())

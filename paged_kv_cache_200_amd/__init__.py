@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     DecodeStep,
     IN_PASS_MERGE_MAX_PARTITIONS,
     append_paged_decode,
+    append_paged_decode_layers,
     append_paged_decode_planned,
     append_paged_decode_static,
     STATIC_SCRATCH_BYTES,

@@ -449,6 +449,69 @@ class DecodeStep:
         return out, lse
 
 
+def append_paged_decode_layers(q, k_cache, v_cache, k_new, v_new, block_tables, start_pos,
+                               cu_new_tokens, context_lens, max_context_len, workspace,
+                               scale=None, partition_size=0, out=None, lse=None, stream=None):
+    """A whole decode step over stacked layers in two library calls: pkv_decode_plan for the
+    step's lengths, then pkv_append_paged_decode_planned_layers (each layer's append +
+    decode in order).  q [L, B, Hq, D], caches [L, NB, Hkv, 16, D], k_new / v_new
+    [L, T, Hkv, D]; out [B, Hq, D] (every layer overwrites it, the last layer's result
+    stays) or [L, B, Hq, D]; lse likewise, or None.  Same results as DecodeStep.layers.
+    The tensors are checked once for the step, the workspace size by the library."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"),
+                 (v_new, "v_new")):
+        _gpu(t, n)
+        _same_kind(k_cache, t, n)
+    if q.dim() != 4 or k_cache.dim() != 5 or k_new.dim() != 4:
+        raise ValueError("stacked tensors expected: q [L, B, Hq, D], caches "
+                         "[L, NB, Hkv, 16, D], k_new / v_new [L, T, Hkv, D]")
+    L, B, hq, d = q.shape
+    _, nb, hkv, bs, dk = k_cache.shape
+    if (v_cache.shape != k_cache.shape or k_cache.shape[0] != L or bs != BLOCK_SIZE
+            or dk != d or v_new.shape != k_new.shape or k_new.shape[0] != L
+            or tuple(k_new.shape[2:]) != (hkv, d)):
+        raise ValueError("q, caches and new K/V must stack the same layers and heads")
+    for t, n in ((block_tables, "block_tables"), (start_pos, "start_pos"),
+                 (cu_new_tokens, "cu_new_tokens"), (context_lens, "context_lens")):
+        _gpu(t, n, torch.int32)
+    if (block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,)
+            or start_pos.shape != (B,) or cu_new_tokens.shape != (B + 1,)):
+        raise ValueError("block_tables [B, W], start_pos / context_lens [B] and "
+                         "cu_new_tokens [B + 1] expected")
+    _gpu(workspace, "workspace")
+    if out is None:
+        raise ValueError("out is required: [B, Hq, D] or [L, B, Hq, D] float32")
+    _gpu(out, "out", torch.float32)
+    if tuple(out.shape) == (B, hq, d):
+        out_stride = 0
+    elif tuple(out.shape) == (L, B, hq, d):
+        out_stride = out.stride(0)
+    else:
+        raise ValueError("out must be [B, Hq, D] or [L, B, Hq, D]")
+    lse_stride = 0
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+        if tuple(lse.shape) == (L, B, hq):
+            lse_stride = lse.stride(0)
+        elif tuple(lse.shape) != (B, hq):
+            raise ValueError("lse must be [B, Hq] or [L, B, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = _stream(stream)
+    W = block_tables.shape[1]
+    _lib.call("pkv_decode_plan", workspace.data_ptr(), wbytes, context_lens.data_ptr(), W, B,
+              hq, d, int(max_context_len), int(partition_size), st)
+    _lib.call("pkv_append_paged_decode_planned_layers", L, out.data_ptr(), out_stride,
+              _ptr(lse), lse_stride, q.data_ptr(), q.stride(0), k_cache.data_ptr(),
+              v_cache.data_ptr(), k_cache.stride(0), k_new.data_ptr(), v_new.data_ptr(),
+              k_new.stride(0), block_tables.data_ptr(), W, start_pos.data_ptr(),
+              cu_new_tokens.data_ptr(), k_new.shape[1], context_lens.data_ptr(), B, hq, hkv,
+              d, BLOCK_SIZE, nb, int(max_context_len), float(scale), int(partition_size),
+              workspace.data_ptr(), wbytes, _kv_code(k_cache), st)
+    return out, lse
+
+
 def paged_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_starts,
                                group_shared_blocks, max_shared_blocks, max_context_len,
                                scale=None, partition_size=0, out=None, lse=None, workspace=None,

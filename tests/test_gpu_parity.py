@@ -738,6 +738,56 @@ def test_decode_step_layers_in_one_call(shape):
         steps[1].layers(q, pools[1][0][:3], pools[1][1], kn, vn)
 
 
+@pytest.mark.parametrize("shape", ["qwen_bf16_P256", "f32_d64_P0"])
+def test_append_paged_decode_layers_equals_decode_step(shape):
+    """append_paged_decode_layers (plan + every layer, two library calls, the stacked
+    tensors checked once) leaves pools, out and lse equal to DecodeStep.layers bit for
+    bit; stacks that disagree are refused on the host."""
+    say(f"append_paged_decode_layers: {shape}")
+    if shape == "qwen_bf16_P256":
+        case, P = config_case("qwen_gqa", 4, layers=3, max_batch=20), 256
+    else:
+        case = build_case("layers2", [1, 16, 17, 300, 190, 33], 12, 12, 64, "f32", seed=11,
+                          layers=3)
+        P = 0
+    ops = _ops()
+    B, L = case.batch, 3
+    conv = bf16_bits if case.kv_dtype == "bf16" else (lambda x: x)
+    rng = np.random.default_rng(17)
+    dims = (L, B, case.num_kv_heads, case.head_dim)
+    kn = dev(conv(rng.standard_normal(dims).astype(np.float32)))
+    vn = dev(conv(rng.standard_normal(dims).astype(np.float32)))
+    start = dev((case.context_lens - 1).astype(np.int32))
+    cu = dev(np.arange(B + 1, dtype=np.int32))
+    tables, ctx = dev(case.block_tables), dev(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    q = dev(np.stack([case.q[l] for l in range(L)]))
+    pools = [(dev(np.stack(case.k_pool[:L])), dev(np.stack(case.v_pool[:L]))) for _ in range(2)]
+    outs = [torch.empty((L, B, case.num_q_heads, case.head_dim), dtype=torch.float32,
+                        device="cuda") for _ in range(2)]
+    lses = [torch.empty((L, B, case.num_q_heads), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    step = ops.DecodeStep(q[0], pools[0][0][0], pools[0][1][0], kn[0], vn[0], tables, start, cu,
+                          ctx, max_ctx, scale=float(case.scale), partition_size=P)
+    step.layers(q, pools[0][0], pools[0][1], kn, vn, out=outs[0], lse=lses[0])
+    ws = torch.empty(ops.decode_workspace_bytes(B, case.num_q_heads, case.head_dim, max_ctx, P),
+                     dtype=torch.uint8, device="cuda")
+    ops.append_paged_decode_layers(q, pools[1][0], pools[1][1], kn, vn, tables, start, cu, ctx,
+                                   max_ctx, ws, scale=float(case.scale), partition_size=P,
+                                   out=outs[1], lse=lses[1])
+    torch.cuda.synchronize()
+    for a, b in ((pools[0][0], pools[1][0]), (pools[0][1], pools[1][1]), (outs[0], outs[1]),
+                 (lses[0], lses[1])):
+        assert a.cpu().numpy().tobytes() == b.cpu().numpy().tobytes()
+    assert_no_device_error()
+    with pytest.raises(ValueError):
+        ops.append_paged_decode_layers(q[:2], pools[1][0], pools[1][1], kn, vn, tables, start,
+                                       cu, ctx, max_ctx, ws, partition_size=P, out=outs[1][0])
+    with pytest.raises(ValueError):
+        ops.append_paged_decode_layers(q, pools[1][0], pools[1][1], kn, vn, tables, start, cu,
+                                       ctx, max_ctx, ws, partition_size=P, out=outs[1][:, :-1])
+
+
 @pytest.mark.parametrize("shape", ["qwen_bf16_P256", "f32_d128_P0"])
 def test_decode_step_equals_planned_calls(shape):
     """DecodeStep (step-wide tensors bound and planned once, one layer() per layer) leaves
