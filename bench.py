@@ -656,10 +656,8 @@ def main():
     settle(run, torch, args.settle_seconds)
     for _ in range(args.warmup):
         run()
-    torch.cuda.synchronize()
-    flags = pkv.device_error()
-    if flags:
-        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
+    # (no device-error read here: it waits on the GPU and would leave it idle, clocks
+    # falling, just before the timed steps; the error word is read after them)
 
     stream = torch.cuda.current_stream()
     t0 = time.perf_counter()
@@ -702,6 +700,9 @@ def main():
             evs[i + 1].record(stream)
         torch.cuda.synchronize()
         per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
     print(f"[bench] {args.steps} steps{' (cold)' if args.cold else ''}: "
           f"{ms_per_step * 1e3:.1f} us/step (wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
