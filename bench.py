@@ -240,10 +240,6 @@ def run_prefill(args, np, torch, pkv):
     settle(step, torch, args.settle_seconds)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    flags = pkv.device_error()
-    if flags:
-        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
     stream = torch.cuda.current_stream()
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -253,6 +249,10 @@ def run_prefill(args, np, torch, pkv):
     e_ev.record(stream)
     torch.cuda.synchronize()
     step_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
+    # the error word is read after the timed steps (the read waits on the GPU)
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
     s_ev.record(stream)
     for _ in range(args.kernel_reps):
         prefill()
