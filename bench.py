@@ -249,16 +249,16 @@ def run_prefill(args, np, torch, pkv):
     e_ev.record(stream)
     torch.cuda.synchronize()
     step_s = s_ev.elapsed_time(e_ev) / 1e3 / args.steps
-    # the error word is read after the timed steps (the read waits on the GPU)
-    flags = pkv.device_error()
-    if flags:
-        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
     s_ev.record(stream)
     for _ in range(args.kernel_reps):
         prefill()
     e_ev.record(stream)
     torch.cuda.synchronize()
     kern_s = s_ev.elapsed_time(e_ev) / 1e3 / args.kernel_reps
+    # the error word is read after the timed launches (the read waits on the GPU)
+    flags = pkv.device_error()
+    if flags:
+        raise RuntimeError(f"device error: {pkv.describe_device_error(flags)}")
     # causal work: query i of a chunk of L at context n attends n - L + i + 1 keys; per key
     # and query head 2 D flops for the score and 2 D for the weighted sum
     keys = 0
