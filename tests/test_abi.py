@@ -91,3 +91,23 @@ def test_decode_step_refuses_host_tensors():
         pkv.DecodeStep(q, kc, kc.clone(), kn, kn.clone(), torch.zeros(B, 4, **i32),
                        torch.zeros(B, **i32), torch.arange(B + 1, **i32), torch.ones(B, **i32),
                        1, partition_size=16)
+
+
+def test_layers_step_refuses_host_tensors():
+    """append_paged_decode_layers checks the step's stacked tensors before it calls the
+    library."""
+    import pytest
+    import torch
+    ensure_built()
+    import paged_kv_cache_200_amd as pkv
+    L, B, hq, hkv, d = 2, 2, 4, 2, 64
+    q = torch.zeros(L, B, hq, d)
+    kc = torch.zeros(L, 8, hkv, 16, d)
+    kn = torch.zeros(L, B, hkv, d)
+    i32 = dict(dtype=torch.int32)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        pkv.append_paged_decode_layers(q, kc, kc.clone(), kn, kn.clone(),
+                                       torch.zeros(B, 4, **i32), torch.zeros(B, **i32),
+                                       torch.arange(B + 1, **i32), torch.ones(B, **i32), 1,
+                                       torch.zeros(4096, dtype=torch.uint8),
+                                       out=torch.zeros(B, hq, d))
